@@ -1,0 +1,187 @@
+/*
+ * attn_sink.h -- C ABI of the sink-aware masked attention forward library
+ * (gfx950 / MI355X).
+ *
+ * One entry point computes, for every packed query row i and query head h,
+ *
+ *     out[i, h, :] = softmax over the key set S(i, h) (plus the sink) of
+ *                    scale * q[i, h, :] . k[j, h / (Hq/Hkv), :]   applied to v
+ *     lse[h, i]    = natural-log log-sum-exp of those scaled logits over the
+ *                    selected keys (never over the null-logit sink)
+ *
+ * Sources (page titles; sections / paragraphs named):
+ *   - "[Bugfix][MiMo] Apply vision attention sinks in the window attention
+ *     path" (vLLM): the symmetric window over cu_seqlens-packed sequences,
+ *     the key0_bias sink (sinks[h] added to the logit of each sequence's first
+ *     key), and the varlen LSE contract of shape (nheads, total_q).
+ *   - "Apply DeepSeek-V4 attn_sink in the XPU sparse-MLA Triton kernel":
+ *     per-row top-k key lists with -1 padding over one shared latent KV, and
+ *     the null_logit sink folded in after the key loop (Implementation
+ *     paragraph): it joins only the softmax denominator, the LSE stays over
+ *     the selected keys, and a sink of -inf leaves the result unchanged.
+ *   - NeMo AutoModel "cp_sparse_attn" API page: a per-query block-selection
+ *     table [B, index_heads, S, key_blocks] combined with token-causal and
+ *     same-document masks (_flex_sparse_attention, _local_sparse_forward),
+ *     fully masked rows giving zero output, and 64-bit table offsets
+ *     (_block_sel_flat_offset).
+ *
+ * Conventions shared by all entry points
+ *   - All tensor data pointers are DEVICE pointers; descriptors themselves
+ *     live in host memory and are read during the call only.
+ *   - Strides are in elements.  The innermost dimension of q, k, v and out must
+ *     be contiguous (stride 1); the other strides are free but must keep every
+ *     row 16-byte aligned (bf16: multiples of 8 elements; f32: of 4).
+ *   - The caller owns every buffer.  The library allocates nothing and keeps no
+ *     mutable global state: calls are reentrant and may run concurrently on
+ *     different streams.  Inputs are read only; out and lse are fully written
+ *     (rows with an empty key set get out = 0 and lse = -inf).
+ *   - Work is enqueued on `stream` as a single kernel launch; the call never
+ *     synchronises and never reads device memory from the host.
+ *   - Errors are returned as negative attn_status codes.  Every argument error
+ *     is detected on the host BEFORE anything is enqueued.  Device-side data
+ *     (cu_seqlens contents, indices) is not validated -- see the
+ *     preconditions below.
+ */
+#ifndef ATTN_SINK_H
+#define ATTN_SINK_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATTN_SINK_ABI_VERSION 1
+
+/* Which key set S(i, h) each query row attends to. */
+typedef enum attn_mask_kind {
+  /* Key j is valid iff it lies in the same cu_seqlens segment as query i and
+   * |i - j| <= window (inclusive; symmetric, not causal).  q and k share the
+   * packed token index space (T == Tk).  MiMo window-attention page. */
+  ATTN_MASK_WINDOW = 0,
+  /* Key j = topk_idx[i, t] for every t with 0 <= topk_idx[i, t] < Tk; any
+   * other entry (-1 by convention) is padding and may sit anywhere in the
+   * row.  One list per row, shared by all heads.  cu_seqlens is ignored.
+   * DeepSeek-V4 sparse-MLA page. */
+  ATTN_MASK_TOPK = 1,
+  /* Key j is valid iff block_sel[0, h / (Hq/Hidx), i, j / block_size] != 0,
+   * j <= i (token causal) and j lies in the same cu_seqlens segment
+   * (document) as i.  T == Tk.  "cp_sparse_attn" page. */
+  ATTN_MASK_BLOCKSEL = 2
+} attn_mask_kind;
+
+/* How sinks[h] enters the softmax. */
+typedef enum attn_sink_mode {
+  ATTN_SINK_NONE = 0,       /* no sink; `sinks` may be NULL                        */
+  /* sinks[h] is added (unscaled) to the scaled logit of the first key of each
+   * cu_seqlens segment whenever that key is in S(i, h); the LSE includes the
+   * biased logit.  Not defined for ATTN_MASK_TOPK (no segments). */
+  ATTN_SINK_KEY0_BIAS = 1,
+  /* out = sum_j e^{l_j} v_j / (e^{sinks[h]} + sum_j e^{l_j}); the LSE is over
+   * the selected keys only; sinks[h] = -inf reproduces ATTN_SINK_NONE bit for
+   * bit. */
+  ATTN_SINK_NULL_LOGIT = 2
+} attn_sink_mode;
+
+typedef enum attn_dtype {
+  ATTN_DTYPE_BF16 = 0,
+  ATTN_DTYPE_F32 = 1,
+  ATTN_DTYPE_I32 = 2,
+  ATTN_DTYPE_U8 = 3
+} attn_dtype;
+
+typedef enum attn_status {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL = -1,        /* a required pointer is NULL                       */
+  ATTN_ERR_ENUM = -2,        /* mask_kind, sink_mode or a dtype is out of range  */
+  ATTN_ERR_SHAPE = -3,       /* ranks or sizes disagree                          */
+  ATTN_ERR_STRIDE = -4,      /* non-unit inner stride or misaligned rows         */
+  ATTN_ERR_HEADS = -5,       /* Hq % Hkv != 0, or Hq % Hidx != 0                 */
+  ATTN_ERR_DTYPE = -6,       /* dtypes disagree or are not allowed for a role    */
+  ATTN_ERR_UNSUPPORTED = -7, /* well-formed, but no kernel instance covers it    */
+  ATTN_ERR_RANGE = -8,       /* a size or value is out of range (T >= 2^31, W<0) */
+  ATTN_ERR_LAUNCH = -9       /* the kernel launch itself failed                  */
+} attn_status;
+
+/* A strided view of a device array (up to 4 dimensions). */
+typedef struct attn_tensor {
+  void* data;          /* device pointer                                 */
+  int32_t dtype;       /* attn_dtype                                     */
+  int32_t ndim;        /* number of used entries in shape / stride       */
+  int64_t shape[4];
+  int64_t stride[4];   /* in elements                                    */
+} attn_tensor;
+
+/* Mask parameters; only the fields of the chosen mask kind are read. */
+typedef struct attn_mask_arg {
+  int32_t window;                /* WINDOW: W >= 0                                   */
+  int32_t block_size;            /* BLOCKSEL: key block size in tokens (> 0)         */
+  const attn_tensor* topk_idx;   /* TOPK: int32 [T, topk], row stride free, inner 1 */
+  const attn_tensor* block_sel;  /* BLOCKSEL: uint8 [1, Hidx, T, NB], NB >= ceil(T/block_size), inner 1 */
+} attn_mask_arg;
+
+/*
+ * attn_sink_fwd -- forward pass; enqueues one kernel on `stream`.
+ *
+ *   q          [T, Hq, Dqk]   bf16 or f32
+ *   k          [Tk, Hkv, Dqk] same dtype as q
+ *   v          [Tk, Hkv, Dv]  same dtype as q; may alias k (shared latent KV:
+ *                             v->data == k->data with the same row stride and
+ *                             Dv <= Dqk reads the first Dv columns of k)
+ *   cu_seqlens device int32 [num_seqs + 1]; required (non-NULL, num_seqs >= 1)
+ *              for WINDOW and BLOCKSEL, ignored for TOPK.
+ *   mask_kind  attn_mask_kind;  mask: its parameters (host struct)
+ *   sinks      device f32 [Hq]; required unless sink_mode == ATTN_SINK_NONE
+ *   sink_mode  attn_sink_mode
+ *   scale      multiplies q.k before the sink is applied (e.g. 1/sqrt(Dqk))
+ *   out        [T, Hq, Dv]    same dtype as q; must not overlap any input
+ *   lse        device f32, dense [Hq, T]; must not overlap any input
+ *   stream     HIP stream the kernel is enqueued on (0 = null stream)
+ *
+ * Kernel instances (anything else returns ATTN_ERR_UNSUPPORTED):
+ *   f32  : every mask kind and sink mode, Dqk <= 576, Dv <= 576 (one wave per
+ *          (row, head); exact-arithmetic reference-grade instance).
+ *   bf16 : WINDOW   Dqk == Dv in {64, 80, 96, 128}, any Hq/Hkv grouping;
+ *          TOPK     shared latent KV (Hkv == 1, v aliasing k), Dqk == 576,
+ *                   Dv == 512, Hq % 64 == 0, sink none / null_logit;
+ *          BLOCKSEL Dqk == Dv == 128, Hq / Hkv == 4, block_size == 64.
+ *   ATTN_SINK_KEY0_BIAS with ATTN_MASK_TOPK is rejected with ATTN_ERR_UNSUPPORTED.
+ *
+ * Device-data preconditions (not checked; checking would need a host sync):
+ *   cu_seqlens is non-decreasing, starts at 0 and ends at T; block_sel entries
+ *   are 0 or 1 (any non-zero byte counts as selected); q, k, v hold finite
+ *   values.  Top-k entries outside [0, Tk) are padding, so any int32 is safe.
+ *
+ * Returns ATTN_OK or a negative attn_status.  T == 0 returns ATTN_OK without
+ * launching.
+ */
+int attn_sink_fwd(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
+                  const int32_t* cu_seqlens, int32_t num_seqs,
+                  int32_t mask_kind, const attn_mask_arg* mask,
+                  const float* sinks, int32_t sink_mode, float scale,
+                  const attn_tensor* out, float* lse, hipStream_t stream);
+
+/*
+ * attn_sink_check -- the host-side argument validation of attn_sink_fwd,
+ * without touching the device: same arguments (no stream), same return code
+ * attn_sink_fwd would give before launching.  Safe to call on a machine
+ * without a GPU.
+ */
+int attn_sink_check(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
+                    const int32_t* cu_seqlens, int32_t num_seqs,
+                    int32_t mask_kind, const attn_mask_arg* mask,
+                    const float* sinks, int32_t sink_mode, float scale,
+                    const attn_tensor* out, const float* lse);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* attn_sink_strerror(int status);
+
+/* ATTN_SINK_ABI_VERSION of the built library. */
+int attn_sink_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_SINK_H */

@@ -1,0 +1,211 @@
+"""Python binding of the sink-aware masked attention forward library (gfx950).
+
+Argument marshalling only: torch tensors supply device pointers, sizes,
+strides and the current HIP stream; every step of the computation runs in the
+HIP kernels of ``libattn_sink.so`` behind the C ABI declared in
+``include/attn_sink.h``.  There is no fallback: if the library is missing the
+import fails, and if a call is rejected the C status is raised.
+
+Names mirror the C ABI: :func:`attn_sink_fwd`, :func:`attn_sink_check`,
+:func:`attn_sink_strerror`, :func:`attn_sink_abi_version`.  :func:`fwd` is the
+same call with keyword arguments that also allocates ``out`` / ``lse``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libattn_sink.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is not built; run `python __graft_entry__.py` (hipcc, gfx950) first")
+_lib = ctypes.CDLL(LIB_PATH)
+
+MASK_KINDS = {"window": 0, "topk": 1, "blocksel": 2}
+SINK_MODES = {"none": 0, "key0_bias": 1, "null_logit": 2}
+DTYPE_BF16, DTYPE_F32, DTYPE_I32, DTYPE_U8 = 0, 1, 2, 3
+STATUS = {0: "ATTN_OK", -1: "ATTN_ERR_NULL", -2: "ATTN_ERR_ENUM", -3: "ATTN_ERR_SHAPE",
+          -4: "ATTN_ERR_STRIDE", -5: "ATTN_ERR_HEADS", -6: "ATTN_ERR_DTYPE",
+          -7: "ATTN_ERR_UNSUPPORTED", -8: "ATTN_ERR_RANGE", -9: "ATTN_ERR_LAUNCH"}
+EXPORTS = ("attn_sink_fwd", "attn_sink_check", "attn_sink_strerror", "attn_sink_abi_version")
+
+
+class AttnTensor(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("ndim", ctypes.c_int32),
+                ("shape", ctypes.c_int64 * 4), ("stride", ctypes.c_int64 * 4)]
+
+
+class AttnMaskArg(ctypes.Structure):
+    _fields_ = [("window", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("topk_idx", ctypes.POINTER(AttnTensor)), ("block_sel", ctypes.POINTER(AttnTensor))]
+
+
+_P = ctypes.c_void_p
+_T = ctypes.POINTER(AttnTensor)
+_lib.attn_sink_fwd.restype = ctypes.c_int
+_lib.attn_sink_fwd.argtypes = [_T, _T, _T, _P, ctypes.c_int32, ctypes.c_int32,
+                               ctypes.POINTER(AttnMaskArg), _P, ctypes.c_int32, ctypes.c_float,
+                               _T, _P, _P]
+_lib.attn_sink_check.restype = ctypes.c_int
+_lib.attn_sink_check.argtypes = [_T, _T, _T, _P, ctypes.c_int32, ctypes.c_int32,
+                                 ctypes.POINTER(AttnMaskArg), _P, ctypes.c_int32, ctypes.c_float,
+                                 _T, _P]
+_lib.attn_sink_strerror.restype = ctypes.c_char_p
+_lib.attn_sink_strerror.argtypes = [ctypes.c_int]
+_lib.attn_sink_abi_version.restype = ctypes.c_int
+_lib.attn_sink_abi_version.argtypes = []
+
+
+class AttnSinkError(RuntimeError):
+    def __init__(self, status: int):
+        self.status = status
+        super().__init__(f"{STATUS.get(status, status)}: {attn_sink_strerror(status)}")
+
+
+def attn_sink_strerror(status: int) -> str:
+    return _lib.attn_sink_strerror(int(status)).decode()
+
+
+def attn_sink_abi_version() -> int:
+    return int(_lib.attn_sink_abi_version())
+
+
+def _dtype_code(t) -> int:
+    import torch
+    codes = {torch.bfloat16: DTYPE_BF16, torch.float32: DTYPE_F32, torch.int32: DTYPE_I32,
+             torch.uint8: DTYPE_U8, torch.bool: DTYPE_U8}
+    if t.dtype not in codes:
+        raise TypeError(f"unsupported tensor dtype {t.dtype}")
+    return codes[t.dtype]
+
+
+def desc(t, *, data=None, dtype=None, shape=None, stride=None) -> AttnTensor:
+    """Descriptor of a torch tensor (or of explicit fields, for host-side checks)."""
+    d = AttnTensor()
+    if t is not None:
+        data = t.data_ptr() if data is None else data
+        dtype = _dtype_code(t) if dtype is None else dtype
+        shape = tuple(t.shape) if shape is None else shape
+        stride = tuple(t.stride()) if stride is None else stride
+    d.data = data
+    d.dtype = dtype
+    d.ndim = len(shape)
+    for i, (s, st) in enumerate(zip(shape, stride)):
+        d.shape[i] = int(s)
+        d.stride[i] = int(st)
+    return d
+
+
+def _ptr(t):
+    return None if t is None else (t if isinstance(t, int) else t.data_ptr())
+
+
+def _ref(x):
+    return None if x is None else ctypes.byref(x)
+
+
+def _as_desc(x):
+    if x is None or isinstance(x, AttnTensor):
+        return x
+    return desc(x)
+
+
+def _mask(mask_kind, window, block_size, topk_idx, block_sel):
+    m = AttnMaskArg()
+    m.window = int(window or 0)
+    m.block_size = int(block_size or 0)
+    ti, bs = _as_desc(topk_idx), _as_desc(block_sel)
+    m.topk_idx = ctypes.pointer(ti) if ti is not None else None
+    m.block_sel = ctypes.pointer(bs) if bs is not None else None
+    return m, (ti, bs)
+
+
+def _codes(mask_kind, sink_mode):
+    mk = MASK_KINDS[mask_kind] if isinstance(mask_kind, str) else int(mask_kind)
+    sm = SINK_MODES[sink_mode] if isinstance(sink_mode, str) else int(sink_mode)
+    return mk, sm
+
+
+def attn_sink_check(q, k, v, cu_seqlens, num_seqs, mask_kind, mask: dict, sinks, sink_mode,
+                    scale, out, lse) -> int:
+    """Host-side validation only (no device access); returns the C status."""
+    mk, sm = _codes(mask_kind, sink_mode)
+    m, keep = _mask(mk, mask.get("window"), mask.get("block_size"), mask.get("topk_idx"),
+                    mask.get("block_sel"))
+    dq, dk, dv, do = (_as_desc(x) for x in (q, k, v, out))
+    return int(_lib.attn_sink_check(_ref(dq), _ref(dk), _ref(dv), _ptr(cu_seqlens), int(num_seqs), mk,
+                                    ctypes.byref(m), _ptr(sinks), sm, float(scale), _ref(do), _ptr(lse)))
+
+
+def attn_sink_fwd(q, k, v, cu_seqlens, mask_kind, mask: dict, sinks, sink_mode, scale, out, lse,
+                  stream=None) -> None:
+    """Enqueue the forward on `stream` (default: torch's current stream on q's device).
+
+    q, k, v, out: torch tensors on the GPU; cu_seqlens: int32 device tensor or
+    None; mask: {"window": W} | {"topk_idx": int32 [T, topk]} |
+    {"block_sel": uint8/bool [1, Hidx, T, NB], "block_size": bs}; sinks: f32
+    device tensor [Hq] or None; lse: f32 device tensor [Hq, T].
+    Raises AttnSinkError on a non-zero status."""
+    import torch
+    mk, sm = _codes(mask_kind, sink_mode)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    m, keep = _mask(mk, mask.get("window"), mask.get("block_size"), mask.get("topk_idx"),
+                    mask.get("block_sel"))
+    num_seqs = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
+    dq, dk, dv, do = desc(q), desc(k), desc(v), desc(out)
+    rc = _lib.attn_sink_fwd(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), _ptr(cu_seqlens),
+                            num_seqs, mk, ctypes.byref(m), _ptr(sinks), sm, float(scale),
+                            ctypes.byref(do), _ptr(lse), ctypes.c_void_p(stream))
+    if rc != 0:
+        raise AttnSinkError(rc)
+
+
+def fwd(q, k, v, *, mask_kind: str, scale: float, cu_seqlens=None, window=None, topk_idx=None,
+        block_sel=None, block_size=None, sinks=None, sink_mode: str = "none", out=None, lse=None,
+        stream=None):
+    """Keyword form of :func:`attn_sink_fwd`; allocates out [T, Hq, Dv] and
+    lse [Hq, T] (float32) with torch when not given.  Returns (out, lse)."""
+    import torch
+    T, Hq = q.shape[0], q.shape[1]
+    if out is None:
+        out = torch.empty((T, Hq, v.shape[2]), dtype=q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((Hq, T), dtype=torch.float32, device=q.device)
+    mask = {"window": window, "topk_idx": topk_idx, "block_sel": block_sel, "block_size": block_size}
+    attn_sink_fwd(q, k, v, cu_seqlens, mask_kind, mask, sinks, sink_mode, scale, out, lse, stream)
+    return out, lse
+
+
+def case_on_device(case: dict, device="cuda:0") -> dict:
+    """Copy a generated input case (NumPy arrays) to device tensors: bf16 or f32
+    values (bit-exact), int32 / uint8 metadata.  The shared-latent layout keeps
+    v as a view of k."""
+    import torch
+    dt = torch.bfloat16 if case["dtype"] == "bf16" else torch.float32
+
+    def t(a, dtype):
+        return None if a is None else torch.from_numpy(a).to(device=device, dtype=dtype)
+
+    q = t(case["q"], dt)
+    k = t(case["k"], dt)
+    if case.get("v_aliases_k"):
+        v = k[:, :, :case["v"].shape[2]]
+    else:
+        v = t(case["v"].copy(), dt)
+    return dict(q=q, k=k, v=v, mask_kind=case["mask_kind"], scale=case["scale"],
+                cu_seqlens=t(case["cu_seqlens"], torch.int32), window=case["window"],
+                topk_idx=t(case["topk_idx"], torch.int32), block_sel=t(case["block_sel"], torch.uint8),
+                block_size=case["block_size"], sinks=t(case["sinks"], torch.float32),
+                sink_mode=case["sink_mode"])
+
+
+def run_case(case: dict, device="cuda:0", **over):
+    """Run a generated case on the GPU; returns (out, lse) device tensors."""
+    d = case_on_device(case, device)
+    d.update(over)
+    return fwd(**d)

@@ -1,0 +1,128 @@
+// Device-side building blocks shared by the gfx950 attention kernels.
+//
+// The kernels compute the masked softmax with a per-head sink in the exp2
+// domain: every logit is multiplied by scale*log2(e) once, the running max and
+// the rescale factors are powers of two of differences of those values, and
+// the natural-log LSE is recovered at the end as ln2 * (m + log2 l).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+typedef __bf16 bf16;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short shortx4;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float floatx4;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+enum SinkMode : int { kSinkNone = 0, kSinkKey0 = 1, kSinkNull = 2 };
+enum MaskKind : int { kMaskWindow = 0, kMaskTopk = 1, kMaskBlocksel = 2 };
+
+// Everything a kernel needs, passed by value.  Strides are in elements.
+struct Params {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  float* lse;
+  const int32_t* cu;
+  const float* sinks;
+  const int32_t* topk_idx;
+  const uint8_t* bsel;
+  int64_t q_row, q_head, k_row, k_head, v_row, v_head, o_row, o_head;
+  int64_t topk_row;
+  int64_t bsel_head, bsel_q;  // strides of block_sel's index-head and query axes
+  int T, Tk, Hq, Hkv, group;  // group = Hq / Hkv
+  int Dqk, Dv;
+  int num_seqs;
+  int window;
+  int topk;
+  int Hidx, NB, block_size;
+  float scale_log2;           // scale * log2(e)
+  int num_tiles;              // query tiles per head (kernel specific)
+};
+
+// ---------------------------------------------------------------- MFMA
+__device__ __forceinline__ floatx4 mfma32(bf16x8 a, bf16x8 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ floatx4 mfma16(bf16x4 a, bf16x4 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+// Transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group, lane
+// j reads 4 consecutive 16-bit values at its own address; the group's 16 x 4
+// values come back transposed so that output lane i, element r, is source
+// lane 4*r + i/4's element i%4.  With source lane j pointing at
+// row (r0 + j/4), column (c0 + 4*(j%4)) of a row-major tile, output lane i
+// receives the column c0 + i of rows r0 .. r0+3.
+__device__ __forceinline__ bf16x4 lds_read_tr4(const bf16* p) {
+  shortx4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (shortx4 __attribute__((address_space(3)))*)(p));
+  return __builtin_bit_cast(bf16x4, v);
+}
+
+__device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b) {
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+__device__ __forceinline__ float exp2f_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// max / sum over the four 16-lane groups holding the same MFMA column
+__device__ __forceinline__ float max_over_groups(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16));
+  return fmaxf(x, __shfl_xor(x, 32));
+}
+__device__ __forceinline__ float sum_over_groups(float x) {
+  x += __shfl_xor(x, 16);
+  return x + __shfl_xor(x, 32);
+}
+
+// Segment s with cu[s] <= t < cu[s+1] (largest such s; empty segments are
+// skipped).  Requires 0 <= t < cu[num_seqs] and cu[0] == 0.
+__device__ __forceinline__ int find_segment(const int32_t* __restrict__ cu, int num_seqs, int t) {
+  int lo = 0, hi = num_seqs - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (__ldg(cu + mid) <= t) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Blocks are dispatched round-robin over the 8 XCDs (block b -> XCD b % 8).
+// Renumber so that each XCD receives one contiguous range of logical blocks:
+// neighbouring tiles, which read overlapping K/V rows, then share an L2.
+__device__ __forceinline__ int xcd_remap(int b, int n) {
+  const int x = b & 7, q = n >> 3, r = n & 7;
+  return x * q + (x < r ? x : r) + (b >> 3);
+}
+
+// The sink fold after the key loop, in the exp2 domain.  Returns the factor
+// that turns the accumulator into the output; m2 / l are the running max and
+// the row sum over the selected keys.  none / key0_bias: 1 / l.
+// null_logit: m' = max(m, s), l' = l * 2^(m - m') + 2^(s - m'), factor
+// 2^(m - m') / l'.  With s = -inf every step is exact (max(m, -inf) = m,
+// 2^0 = 1, + 0) and the factor is bitwise the no-sink one.  Empty rows (l == 0)
+// give 0.
+template <int SINK>
+__device__ __forceinline__ float sink_fold(float m2, float l, float sink_log2) {
+  float alpha = 1.0f, ltot = l;
+  if (SINK == kSinkNull) {
+    const float mn = fmaxf(m2, sink_log2);
+    alpha = exp2f_fast(m2 - mn);
+    ltot = l * alpha + exp2f_fast(sink_log2 - mn);
+  }
+  return l > 0.0f ? alpha / ltot : 0.0f;
+}
+
+__device__ __forceinline__ float lse_natural(float m2, float l) {
+  return l > 0.0f ? (m2 + __log2f(l)) * kLn2 : kNegInf;
+}
+
+}  // namespace attn

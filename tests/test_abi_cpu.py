@@ -1,0 +1,170 @@
+"""The C-ABI library on a host without a GPU: it loads, exports exactly what
+include/attn_sink.h declares, and its host-side validation accepts every
+supported call and rejects each class of bad argument with the documented
+status (no device access: attn_sink_check never touches memory)."""
+from __future__ import annotations
+
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn_sink.h")
+
+
+@pytest.fixture(scope="module")
+def sam():
+    lib = os.path.join(ROOT, "sink_aware_masked_amd", "libattn_sink.so")
+    if not os.path.exists(lib):
+        import __graft_entry__
+        __graft_entry__.build_library()
+    import sink_aware_masked_amd
+    return sink_aware_masked_amd
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(attn_sink_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_exports_match_header(sam):
+    decl = declared_functions()
+    assert decl == sorted(sam.EXPORTS)
+    for name in decl:
+        assert hasattr(sam._lib, name), name
+    nm = subprocess.run(["nm", "-D", "--defined-only", sam.LIB_PATH], capture_output=True, text=True, check=True)
+    exported = sorted(ln.split()[-1] for ln in nm.stdout.splitlines() if " T " in ln and ln.split()[-1].startswith("attn_"))
+    assert exported == decl
+
+
+def test_version_and_strerror(sam):
+    m = re.search(r"#define ATTN_SINK_ABI_VERSION (\d+)", open(HEADER).read())
+    assert sam.attn_sink_abi_version() == int(m.group(1))
+    for code in list(sam.STATUS) + [-100, 7]:
+        s = sam.attn_sink_strerror(code)
+        assert isinstance(s, str) and s
+    assert sam.attn_sink_strerror(0) == "ok"
+
+
+# ------------------------------------------------------------ validation
+def window_args(T=256, Hq=16, Hkv=4, D=80, dtype=torch.bfloat16, W=64, sink="key0_bias"):
+    q = torch.empty(T, Hq, D, dtype=dtype)
+    k = torch.empty(T, Hkv, D, dtype=dtype)
+    v = torch.empty(T, Hkv, D, dtype=dtype)
+    out = torch.empty(T, Hq, D, dtype=dtype)
+    lse = torch.empty(Hq, T, dtype=torch.float32)
+    cu = torch.tensor([0, 100, T], dtype=torch.int32)
+    sinks = torch.zeros(Hq, dtype=torch.float32)
+    return dict(q=q, k=k, v=v, cu_seqlens=cu, num_seqs=2, mask_kind="window", mask={"window": W},
+                sinks=sinks, sink_mode=sink, scale=0.1, out=out, lse=lse)
+
+
+def mla_args(T=8, Hq=64, Tk=100, topk=16):
+    q = torch.empty(T, Hq, 576, dtype=torch.bfloat16)
+    kv = torch.empty(Tk, 1, 576, dtype=torch.bfloat16)
+    return dict(q=q, k=kv, v=kv[:, :, :512], cu_seqlens=None, num_seqs=0, mask_kind="topk",
+                mask={"topk_idx": torch.empty(T, topk, dtype=torch.int32)},
+                sinks=torch.zeros(Hq), sink_mode="null_logit", scale=0.04,
+                out=torch.empty(T, Hq, 512, dtype=torch.bfloat16), lse=torch.empty(Hq, T))
+
+
+def bsel_args(T=300, Hq=32, Hkv=8, D=128, bs=64):
+    NB = (T + bs - 1) // bs
+    return dict(q=torch.empty(T, Hq, D, dtype=torch.bfloat16), k=torch.empty(T, Hkv, D, dtype=torch.bfloat16),
+                v=torch.empty(T, Hkv, D, dtype=torch.bfloat16), cu_seqlens=torch.tensor([0, 120, T], dtype=torch.int32),
+                num_seqs=2, mask_kind="blocksel",
+                mask={"block_sel": torch.empty(1, Hkv, T, NB, dtype=torch.uint8), "block_size": bs},
+                sinks=None, sink_mode="none", scale=0.088, out=torch.empty(T, Hq, D, dtype=torch.bfloat16),
+                lse=torch.empty(Hq, T))
+
+
+def check(sam, a):
+    return sam.attn_sink_check(a["q"], a["k"], a["v"], a["cu_seqlens"], a["num_seqs"], a["mask_kind"], a["mask"],
+                               a["sinks"], a["sink_mode"], a["scale"], a["out"], a["lse"])
+
+
+@pytest.mark.parametrize("D", [64, 80, 96, 128])
+@pytest.mark.parametrize("sink", ["none", "key0_bias", "null_logit"])
+def test_supported_window(sam, D, sink):
+    assert check(sam, window_args(D=D, sink=sink)) == 0
+
+
+def test_supported_others(sam):
+    assert check(sam, mla_args()) == 0
+    assert check(sam, bsel_args()) == 0
+    a = bsel_args()
+    a.update(sink_mode="null_logit", sinks=torch.zeros(32))
+    assert check(sam, a) == 0
+    for kind, args in (("window", window_args(D=48, dtype=torch.float32)),):
+        assert check(sam, args) == 0
+    f = mla_args()
+    for key in ("q", "k", "out"):
+        f[key] = f[key].float()
+    f["v"] = f["k"][:, :, :512]
+    assert check(sam, f) == 0
+    e = window_args(T=0)
+    e["cu_seqlens"] = torch.tensor([0], dtype=torch.int32)
+    e["num_seqs"] = 0
+    assert check(sam, e) == 0
+
+
+def _bad(sam, base, expect, **over):
+    a = dict(base)
+    a.update(over)
+    rc = check(sam, a)
+    assert sam.STATUS[rc] == expect, (sam.STATUS.get(rc), expect, over.keys())
+
+
+def test_rejections(sam):
+    E = sam
+    w = window_args()
+    _bad(E, w, "ATTN_ERR_NULL", q=None)
+    _bad(E, w, "ATTN_ERR_NULL", lse=None)
+    _bad(E, w, "ATTN_ERR_NULL", sinks=None)
+    _bad(E, w, "ATTN_ERR_NULL", cu_seqlens=None)
+    _bad(E, w, "ATTN_ERR_ENUM", mask_kind=3)
+    _bad(E, w, "ATTN_ERR_ENUM", sink_mode=-1)
+    _bad(E, w, "ATTN_ERR_SHAPE", k=torch.empty(255, 4, 80, dtype=torch.bfloat16))
+    _bad(E, w, "ATTN_ERR_SHAPE", out=torch.empty(256, 16, 64, dtype=torch.bfloat16))
+    _bad(E, w, "ATTN_ERR_SHAPE", q=torch.empty(256, 16, 80, 1, dtype=torch.bfloat16))
+    _bad(E, w, "ATTN_ERR_HEADS", k=torch.empty(256, 3, 80, dtype=torch.bfloat16),
+         v=torch.empty(256, 3, 80, dtype=torch.bfloat16))
+    _bad(E, w, "ATTN_ERR_DTYPE", out=torch.empty(256, 16, 80, dtype=torch.float32))
+    _bad(E, w, "ATTN_ERR_DTYPE", q=torch.empty(256, 16, 80, dtype=torch.int32))
+    _bad(E, w, "ATTN_ERR_STRIDE", q=torch.empty(256, 80, 16, dtype=torch.bfloat16).transpose(1, 2))
+    _bad(E, w, "ATTN_ERR_STRIDE", q=torch.empty(256, 16, 84, dtype=torch.bfloat16)[:, :, :80])
+    _bad(E, w, "ATTN_ERR_RANGE", mask={"window": -1})
+    _bad(E, w, "ATTN_ERR_RANGE", scale=float("nan"))
+    _bad(E, w, "ATTN_ERR_UNSUPPORTED", **{k_: torch.empty(256, h, 48, dtype=torch.bfloat16)
+                                         for k_, h in (("q", 16), ("k", 4), ("v", 4), ("out", 16))})
+    m = mla_args()
+    _bad(E, m, "ATTN_ERR_UNSUPPORTED", sink_mode="key0_bias")
+    _bad(E, m, "ATTN_ERR_UNSUPPORTED", v=torch.empty(100, 1, 512, dtype=torch.bfloat16))
+    _bad(E, m, "ATTN_ERR_DTYPE", mask={"topk_idx": torch.empty(8, 16, dtype=torch.float32)})
+    _bad(E, m, "ATTN_ERR_SHAPE", mask={"topk_idx": torch.empty(9, 16, dtype=torch.int32)})
+    _bad(E, m, "ATTN_ERR_NULL", mask={})
+    b = bsel_args()
+    _bad(E, b, "ATTN_ERR_SHAPE", mask={"block_sel": torch.empty(1, 8, 300, 4, dtype=torch.uint8), "block_size": 64})
+    _bad(E, b, "ATTN_ERR_HEADS", mask={"block_sel": torch.empty(1, 3, 300, 5, dtype=torch.uint8), "block_size": 64})
+    _bad(E, b, "ATTN_ERR_RANGE", mask={"block_sel": torch.empty(1, 8, 300, 5, dtype=torch.uint8), "block_size": 0})
+    _bad(E, b, "ATTN_ERR_DTYPE", mask={"block_sel": torch.empty(1, 8, 300, 5, dtype=torch.int32), "block_size": 64})
+    _bad(E, b, "ATTN_ERR_UNSUPPORTED", mask={"block_sel": torch.empty(1, 8, 300, 10, dtype=torch.uint8), "block_size": 32})
+    _bad(E, b, "ATTN_ERR_SHAPE", k=torch.empty(301, 8, 128, dtype=torch.bfloat16),
+         v=torch.empty(301, 8, 128, dtype=torch.bfloat16))
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    """Importing the binding from a copy of the package without the built
+    library raises instead of falling back to anything."""
+    import shutil
+    import sys
+    pkg = tmp_path / "sink_aware_masked_amd"
+    pkg.mkdir()
+    shutil.copy(os.path.join(ROOT, "sink_aware_masked_amd", "__init__.py"), pkg / "__init__.py")
+    code = "import sink_aware_masked_amd"
+    r = subprocess.run([sys.executable, "-c", code], cwd=tmp_path, capture_output=True, text=True)
+    assert r.returncode != 0 and "not built" in r.stderr
