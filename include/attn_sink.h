@@ -145,7 +145,9 @@ typedef struct attn_mask_arg {
  *   bf16 : WINDOW   Dqk == Dv in {64, 80, 96, 128}, any Hq/Hkv grouping;
  *          TOPK     shared latent KV (Hkv == 1, v aliasing k), Dqk == 576,
  *                   Dv == 512, Hq % 64 == 0, sink none / null_logit;
- *          BLOCKSEL Dqk == Dv == 128, Hq / Hkv == 4, block_size == 64.
+ *          BLOCKSEL Dqk == Dv == 128, Hq / Hkv == 4, block_size == 64, and
+ *                   Hkv % Hidx == 0 (the query heads of one kv head share one
+ *                   index head).
  *   ATTN_SINK_KEY0_BIAS with ATTN_MASK_TOPK is rejected with ATTN_ERR_UNSUPPORTED.
  *
  * Device-data preconditions (not checked; checking would need a host sync):

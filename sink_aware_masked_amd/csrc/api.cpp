@@ -164,7 +164,8 @@ int prepare(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
     *inst = kInstTopkMlaBf16;
     return ATTN_OK;
   }
-  if (Dqk != 128 || Dv != 128 || Hq / Hkv != 4 || mask->block_size != 64) return ATTN_ERR_UNSUPPORTED;
+  if (Dqk != 128 || Dv != 128 || Hq / Hkv != 4 || mask->block_size != 64 || Hkv % P->Hidx != 0)
+    return ATTN_ERR_UNSUPPORTED;
   *inst = kInstBlockselBf16;
   return ATTN_OK;
 }

@@ -1,0 +1,103 @@
+"""GPU parity of the block-selection mask (token causal + same document)
+against the CPU oracle, including a table whose offsets pass 2**31."""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+
+import workloads as W
+from tests import gpu_util as G
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+@pytest.mark.parametrize("sink", ["none", "null_logit"])
+def test_blocksparse_32k_sampled(seed, sink):
+    """Full-size block-sparse workload (32768 tokens, 4 documents, 32/8 heads,
+    d128, 64-token blocks) in the benchmark's launch configuration; oracle on
+    sampled rows including every document's first and last tokens."""
+    case = W.make_workload("blocksparse_32k", seed=seed, sink_mode=sink)
+    rows = G.sample_rows(case, 400, seed=seed)
+    G.assert_parity(case, rows=rows, label=f"blocksparse_32k {sink} seed{seed}")
+
+
+SMALL = [
+    # (doc_lens, Hq, Hkv, Hidx, n_random, sink)
+    ([300], 4, 1, 1, 2, "none"),
+    ([130, 70, 250], 8, 2, 2, 3, "null_logit"),
+    ([64, 64, 64], 4, 1, 1, 0, "key0_bias"),          # diagonal blocks only
+    ([1, 2, 500, 3], 16, 4, 4, 5, "key0_bias"),        # tiny documents
+    ([900, 77], 32, 8, 2, 6, "null_logit"),            # index heads shared by 4 kv heads
+    ([2000], 8, 2, 2, 40, "none"),                     # more random blocks than a word
+]
+
+
+@pytest.mark.parametrize("idx", range(len(SMALL)))
+def test_blocksel_small(idx):
+    lens, Hq, Hkv, Hidx, nr, sink = SMALL[idx]
+    case = W.blocksel_case(lens, Hq, Hkv, 128, block_size=64, n_random=nr, Hidx=Hidx, sink_mode=sink,
+                           sink_range=(-2, 2), seed=idx)
+    G.assert_parity(case, label=f"blocksel lens={lens} Hq={Hq} Hkv={Hkv} Hidx={Hidx} nr={nr} {sink}")
+
+
+def test_blocksel_empty_and_dense_rows():
+    """Rows whose table row is all zero are empty (out 0, lse -inf); a full
+    table is plain causal attention inside each document."""
+    case = W.blocksel_case([200, 190], 8, 2, 128, n_random=2, sink_mode="null_logit", seed=11)
+    tab = case["block_sel"].copy()
+    tab[:, :, ::3, :] = 0
+    G.assert_parity(dict(case, block_sel=tab), label="blocksel empty rows")
+    G.assert_parity(dict(case, block_sel=np.ones_like(tab)), label="blocksel dense causal")
+
+
+def test_blocksel_count_and_membership():
+    case = W.blocksel_case([150, 99, 140], 4, 1, 128, n_random=2, sink_mode="none", seed=12)
+    q0 = np.zeros_like(case["q"])
+    _, lse = G.gpu_run(dict(case, q=q0))
+    from tests import pins as P
+    for i in range(case["q"].shape[0]):
+        for h in range(4):
+            n = P.closed_form_count(case, i, h)
+            assert np.rint(np.exp(lse[h, i])) == n, (i, h)
+    T = case["q"].shape[0]
+    mask = P.loop_mask(case, 0)
+    for j in (0, 63, 64, 149, 150, 151, 248, 249, 250, 300, 388):
+        v = np.zeros_like(case["v"])
+        v[j, 0, 0] = 1.0
+        out, _ = G.gpu_run(dict(case, q=q0, v=v))
+        got = out[:, :, 0] != 0
+        assert np.array_equal(got, np.repeat(mask[:, j][:, None], 4, axis=1)), j
+    assert T == 389
+
+
+def test_blocksel_table_offsets_past_2_31():
+    """The block-selection table is a strided view whose second index head
+    starts 2**31 + 4096 bytes into the allocation: every lookup for that head
+    lands past 2**31 and is correct only with 64-bit offsets (NeMo
+    "cp_sparse_attn" page, _block_sel_flat_offset)."""
+    import torch
+    case = W.blocksel_case([700, 324], 8, 2, 128, n_random=4, Hidx=2, sink_mode="null_logit", seed=13)
+    tab = case["block_sel"]                                   # [1, 2, T, NB]
+    T, NB = tab.shape[2], tab.shape[3]
+    head_stride = 2 ** 31 + 4096
+    big = torch.zeros(head_stride + T * NB, dtype=torch.uint8, device="cuda:0")
+    big[:T * NB] = torch.from_numpy(tab[0, 0].reshape(-1)).cuda()
+    big[head_stride:head_stride + T * NB] = torch.from_numpy(tab[0, 1].reshape(-1)).cuda()
+    view = big.as_strided((1, 2, T, NB), (2 * head_stride, head_stride, NB, 1))
+    out, lse = G.gpu_run(case, block_sel=view)
+    ref_o, ref_l = G.oracle_run(case)
+    rel, dl = G.compare(out, lse, ref_o, ref_l)
+    G.say(f"[blocksel >2^31 offsets] rel {rel:.3e} lse {dl:.3e}")
+    assert rel <= G.BF16_REL_L2 and dl <= G.BF16_LSE_ABS
+    del big, view
+    torch.cuda.empty_cache()
+    assert math.isfinite(rel)
+
+
+def test_blocksel_f32_instance():
+    case = W.blocksel_case([90, 41], 4, 2, 32, block_size=16, n_random=3, Hidx=1, dtype="f32",
+                           sink_mode="key0_bias", sink_range=(-2, 2), seed=14)
+    G.assert_parity(case, label="f32 blocksel")
