@@ -1,0 +1,316 @@
+#!/usr/bin/env python3
+"""Benchmark of the sink-aware masked attention forward on one MI355X.
+
+One step = one attn_sink_fwd call (the whole hot path: varlen scheduling, key
+enumeration, K/V staging, logits, online softmax, output accumulation and the
+sink epilogue -- one kernel launch) over one batch of seeded synthetic input
+that is already resident in HBM.
+
+Default workload (no flags): the MiMo vision window block -- 4096 tokens
+packed as 2 x 2048, 16 heads, head dim 80, window 64, bf16, key0_bias sinks
+drawn from U(-0.1, 0.6) -- the shape of the timing paragraph of the vLLM page
+"[Bugfix][MiMo] Apply vision attention sinks in the window attention path".
+Other workloads: --workload window_16k | mla_topk | blocksparse_32k.
+
+Prints ONE JSON line:
+  value      useful TFLOP/s of the whole job = 2 (Dqk + Dv) sum |S(i,h)| / wall time
+  roofline   the kernel against its binding roof, from HIP events on the
+             launch stream (algorithmic bytes or useful flops per launch /
+             average launch duration)
+  cpu_baseline  the CPU oracle (C, fp64, OpenMP) on a bounded row sample of
+             the same workload, in the same unit
+Cold cache: the step rotates over enough input sets to exceed the 256 MB
+Infinity Cache when one set is smaller than that.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "ms/call + useful TFLOP/s (frac of MFMA bf16 peak) for sink-aware masked attn fwd"
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, published
+PEAK_MFMA_BF16_TFS = 2500.0  # MI355X dense bf16 MFMA, published
+MALL_BYTES = 256 << 20       # Infinity Cache
+
+# The pages' timing context (H100, FlashAttention varlen + the unfused key-0
+# correction): ms per call for the same window workloads.
+PAGE_MS = {("window_4k", "key0_bias"): 0.248, ("window_4k", "none"): 0.038,
+           ("window_16k", "key0_bias"): 0.289, ("window_16k", "none"): 0.134}
+
+KERNEL_SRC = {"window": "window_fwd.hip", "topk": "topk_mla_fwd.hip", "blocksel": "blocksel_fwd.hip"}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------- work accounting
+def seg_starts_ends(cu, n):
+    cu = np.asarray(cu, dtype=np.int64)
+    lens = np.diff(cu)
+    return np.repeat(cu[:-1], lens)[:n], np.repeat(cu[1:], lens)[:n]
+
+
+def pairs_per_row(case) -> np.ndarray:
+    """|S(i,h)| summed over heads, per query row (int64 [T])."""
+    T, Hq = case["q"].shape[:2]
+    kind = case["mask_kind"]
+    if kind == "window":
+        st, en = seg_starts_ends(case["cu_seqlens"], T)
+        i = np.arange(T)
+        W = case["window"]
+        return (np.minimum(en - 1, i + W) - np.maximum(st, i - W) + 1) * Hq
+    if kind == "topk":
+        idx = case["topk_idx"]
+        return ((idx >= 0) & (idx < case["k"].shape[0])).sum(1).astype(np.int64) * Hq
+    tab = case["block_sel"][0]                       # [Hidx, T, NB]
+    Hidx, _, NB = tab.shape
+    bs = case["block_size"]
+    st, _ = seg_starts_ends(case["cu_seqlens"], T)
+    i = np.arange(T)[:, None]
+    b0 = (np.arange(NB) * bs)[None, :]
+    ov = np.clip(np.minimum(i, b0 + bs - 1) - np.maximum(st[:, None], b0) + 1, 0, None)
+    out = np.zeros(T, dtype=np.int64)
+    for h in range(Hidx):
+        out += ((tab[h] != 0) * ov).sum(1)
+    return out * (Hq // Hidx)
+
+
+def algorithmic_bytes(case) -> int:
+    q, k, v = case["q"], case["k"], case["v"]
+    T, Hq, Dqk = q.shape
+    Tk, Hkv, _ = k.shape
+    Dv = v.shape[2]
+    es = 2 if case["dtype"] == "bf16" else 4
+    b = T * Hq * Dqk * es + T * Hq * Dv * es + Hq * T * 4
+    kind = case["mask_kind"]
+    if kind == "window":
+        b += Tk * Hkv * (Dqk + Dv) * es + case["cu_seqlens"].nbytes
+    elif kind == "topk":
+        idx = case["topk_idx"]
+        distinct = np.unique(idx[(idx >= 0) & (idx < Tk)]).size
+        row = Dqk * es if case.get("v_aliases_k") else (Dqk + Dv) * es
+        b += distinct * Hkv * row + idx.nbytes
+    else:
+        tab = case["block_sel"][0]
+        used = (tab != 0).any(axis=1)                # [Hidx, NB] blocks any query selected
+        bs = case["block_size"]
+        keys_per_idx = np.minimum((np.arange(used.shape[1]) + 1) * bs, Tk) - np.arange(used.shape[1]) * bs
+        keys = (used * keys_per_idx[None, :]).sum(1)  # per index head
+        b += int(keys.sum()) * (Hkv // tab.shape[0]) * (Dqk + Dv) * es + case["block_sel"].nbytes
+        b += case["cu_seqlens"].nbytes
+    if case["sinks"] is not None:
+        b += Hq * 4
+    return int(b)
+
+
+def kernel_hash(kind: str) -> str:
+    h = hashlib.sha256()
+    for f in ("common.hpp", KERNEL_SRC[kind]):
+        h.update(open(os.path.join(ROOT, "sink_aware_masked_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str, kind: str):
+    """HBM bytes per launch from committed rocprofv3 PMC counters, or None if
+    absent or taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("kernel_sha") != kernel_hash(kind):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+# ----------------------------------------------------------------- workloads
+def build_case(name: str, seed: int, sink_mode: str | None):
+    import workloads as W
+    kw = {} if sink_mode is None else {"sink_mode": sink_mode}
+    return W.make_workload(name, seed=seed, **kw)
+
+
+def describe(name, case, sets):
+    q, k, v = case["q"], case["k"], case["v"]
+    cfg = {"workload": name, "tokens": int(q.shape[0]), "q_heads": int(q.shape[1]),
+           "kv_heads": int(k.shape[1]), "head_dim_qk": int(q.shape[2]), "head_dim_v": int(v.shape[2]),
+           "mask": case["mask_kind"], "sink_mode": case["sink_mode"], "cold_cache_sets": sets}
+    if case["mask_kind"] == "window":
+        cfg.update(window=case["window"], seqs=len(case["cu_seqlens"]) - 1)
+    elif case["mask_kind"] == "topk":
+        cfg.update(kv_entries=int(k.shape[0]), topk=int(case["topk_idx"].shape[1]), shared_latent_kv=True)
+    else:
+        cfg.update(documents=len(case["cu_seqlens"]) - 1, block_size=case["block_size"],
+                   index_heads=int(case["block_sel"].shape[1]))
+    return cfg
+
+
+# ------------------------------------------------------------------- timing
+def time_gpu(case, sets_n, steps, warmup):
+    import torch
+    import sink_aware_masked_amd as sam
+    torch.cuda.set_device(0)
+    calls, keep = [], []
+    for _ in range(sets_n):
+        d = sam.case_on_device(case, "cuda:0")
+        T, Hq = d["q"].shape[:2]
+        d["out"] = torch.empty((T, Hq, d["v"].shape[2]), dtype=d["q"].dtype, device="cuda:0")
+        d["lse"] = torch.empty((Hq, T), dtype=torch.float32, device="cuda:0")
+        calls.append(sam.prepared_fwd(**d))
+        keep.append(d)
+    for s in range(warmup):
+        calls[s % sets_n]()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()                                   # barrier: N = 1
+    t0 = time.perf_counter()
+    for s in range(steps):
+        ev[s][0].record()
+        calls[s % sets_n]()
+        ev[s][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    durs = np.array([a.elapsed_time(b) for a, b in ev])        # ms, per launch
+    return wall * 1e3 / steps, durs, keep[0]
+
+
+def cpu_baseline(case, pairs_row, dqk_dv, budget_s, out_dev, lse_dev):
+    """The oracle as it stands, on a seeded row sample sized to ~budget_s."""
+    import oracle
+    T = case["q"].shape[0]
+    g = np.random.default_rng(1234)
+    kw = dict(mask_kind=case["mask_kind"], scale=case["scale"], cu_seqlens=case["cu_seqlens"],
+              window=case["window"], topk_idx=case["topk_idx"], block_sel=case["block_sel"],
+              block_size=case["block_size"], sinks=case["sinks"], sink_mode=case["sink_mode"])
+    probe = np.sort(g.choice(T, size=min(T, 64), replace=False))
+    t = time.perf_counter()
+    oracle.attn_ref(case["q"], case["k"], case["v"], rows=probe, **kw)
+    per_pair = max(time.perf_counter() - t, 1e-4) / max(1, int(pairs_row[probe].sum()))
+    want_pairs = budget_s / per_pair
+    order = g.permutation(T)
+    csum = np.cumsum(pairs_row[order])
+    n = int(min(T, max(64, np.searchsorted(csum, want_pairs) + 1)))
+    rows = np.sort(order[:n])
+    t = time.perf_counter()
+    ref_o, ref_l = oracle.attn_ref(case["q"], case["k"], case["v"], rows=rows, **kw)
+    secs = time.perf_counter() - t
+    flops = 2.0 * dqk_dv * float(pairs_row[rows].sum())
+    out = out_dev.float().cpu().numpy().astype(np.float64)[rows]
+    lse = lse_dev.cpu().numpy().astype(np.float64)[:, rows]
+    fin = np.isfinite(ref_l.T)
+    ref_n = np.linalg.norm(ref_o, axis=2)
+    nz = fin & (ref_n > 0)
+    rel = float((np.linalg.norm(out - ref_o, axis=2)[nz] / ref_n[nz]).max()) if nz.any() else 0.0
+    dl = float(np.abs(lse.T[fin] - ref_l.T[fin]).max()) if fin.any() else 0.0
+    assert np.all(out[~fin] == 0.0) and np.all(np.isneginf(lse.T[~fin]))
+    return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{n} of {T} query rows (all heads), seeded; {secs:.1f} s wall; fp64 C enumerator",
+            "ms_per_call_equiv": secs * 1e3 * float(pairs_row.sum()) / float(pairs_row[rows].sum())}, \
+        {"max_rel_l2": rel, "lse_max_abs": dl, "rows_checked": n}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="window_4k",
+                    choices=["window_4k", "window_16k", "mla_topk", "blocksparse_32k"])
+    ap.add_argument("--sink-mode", default=None, choices=[None, "none", "key0_bias", "null_logit"])
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--sets", type=int, default=0, help="input sets to rotate (0: enough to exceed the MALL)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle sample budget (0: skip)")
+    ap.add_argument("--compare-sink-none", action="store_true",
+                    help="also time the same workload without a sink and report the ratio")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="also run a plain device copy of this size (PMC scaling reference)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): this build has no multi-GPU path; "
+              "run with --gpus 1", file=sys.stderr)
+        return 2
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    lib = os.path.join(ROOT, "sink_aware_masked_amd", "libattn_sink.so")
+    if not os.path.exists(lib):
+        import __graft_entry__
+        __graft_entry__.build()
+
+    log(f"[bench] building workload {args.workload} seed {args.seed}")
+    case = build_case(args.workload, args.seed, args.sink_mode)
+    prow = pairs_per_row(case)
+    dqk, dv = case["q"].shape[2], case["v"].shape[2]
+    F = 2.0 * (dqk + dv) * float(prow.sum())
+    B = algorithmic_bytes(case)
+    sets_n = args.sets or max(1, min(16, math.ceil(1.25 * MALL_BYTES / B)))
+    log(f"[bench] useful FLOPs {F:.4e}, algorithmic bytes {B:.4e}, sets {sets_n}")
+
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        a = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy of {args.calibrate_copy} MiB done")
+
+    log(f"[bench] timing {args.steps} steps after {args.warmup} warmup")
+    ms, durs, dev0 = time_gpu(case, sets_n, args.steps, args.warmup)
+    kern_ms = float(durs.mean())
+    kind = case["mask_kind"]
+    bound = "hbm" if kind == "window" else "mfma"
+    if bound == "hbm":
+        ach = B / (kern_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": ach / PEAK_HBM_GBS}
+    else:
+        ach = F / (kern_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": ach, "peak": PEAK_MFMA_BF16_TFS, "unit": "TFLOP/s",
+                "frac": ach / PEAK_MFMA_BF16_TFS}
+    roof["traffic"] = load_traffic(args.workload + ":" + case["sink_mode"], kind)
+    roof["kernel_ms"] = kern_ms
+    roof["kernel_ms_p10_p90"] = [float(np.percentile(durs, 10)), float(np.percentile(durs, 90))]
+    roof["algorithmic_bytes"] = B
+    roof["useful_flops"] = F
+
+    value = F / (ms * 1e-3) / 1e12
+    page = PAGE_MS.get((args.workload, case["sink_mode"]))
+    res = {"metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": (page / ms) if page else None, "dtype": case["dtype"], "data": "synthetic",
+           "config": describe(args.workload, case, sets_n), "roofline": roof}
+
+    if args.compare_sink_none and case["sink_mode"] != "none":
+        base = dict(case, sink_mode="none", sinks=None)
+        ms0, durs0, _ = time_gpu(base, sets_n, args.steps, args.warmup)
+        res["sink_vs_none"] = {"kernel_ms_sink": kern_ms, "kernel_ms_none": float(durs0.mean()),
+                               "ratio": kern_ms / float(durs0.mean()), "ms_per_step_none": ms0}
+
+    if args.cpu_seconds > 0:
+        log(f"[bench] CPU oracle baseline (~{args.cpu_seconds:.0f} s)")
+        cb, parity = cpu_baseline(case, prow, dqk + dv, args.cpu_seconds, dev0["out"], dev0["lse"])
+        res["cpu_baseline"] = cb
+        res["parity_sample"] = parity
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -165,6 +165,35 @@ def attn_sink_fwd(q, k, v, cu_seqlens, mask_kind, mask: dict, sinks, sink_mode, 
         raise AttnSinkError(rc)
 
 
+def prepared_fwd(q, k, v, *, mask_kind: str, scale: float, out, lse, cu_seqlens=None, window=None,
+                 topk_idx=None, block_sel=None, block_size=None, sinks=None, sink_mode: str = "none",
+                 stream=None):
+    """Marshal the arguments once and return a zero-argument callable that
+    re-issues the same attn_sink_fwd call (for timing loops and graph capture,
+    where per-call Python marshalling would dominate a microsecond kernel)."""
+    import torch
+    mk, sm = _codes(mask_kind, sink_mode)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    m, keep = _mask(mk, window, block_size, topk_idx, block_sel)
+    num_seqs = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
+    dq, dk, dv, do = desc(q), desc(k), desc(v), desc(out)
+    args = (ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), _ptr(cu_seqlens), num_seqs, mk,
+            ctypes.byref(m), _ptr(sinks), sm, float(scale), ctypes.byref(do), _ptr(lse),
+            ctypes.c_void_p(stream))
+    hold = (dq, dk, dv, do, m, keep, q, k, v, out, lse, cu_seqlens, sinks, topk_idx, block_sel)
+    fn = _lib.attn_sink_fwd
+
+    def call():
+        rc = fn(*args)
+        if rc != 0:
+            raise AttnSinkError(rc)
+    call._hold = hold
+    return call
+
+
 def fwd(q, k, v, *, mask_kind: str, scale: float, cu_seqlens=None, window=None, topk_idx=None,
         block_sel=None, block_size=None, sinks=None, sink_mode: str = "none", out=None, lse=None,
         stream=None):
