@@ -55,12 +55,17 @@ int check_tensor(const attn_tensor* t, int ndim) {
   return ATTN_OK;
 }
 
-// Rows of [rows, heads, dim] tensors must start on 16-byte boundaries.
+// Rows of [rows, heads, dim] tensors must start on 16-byte boundaries, must
+// not overlap (a row stride of at least the head dim), and one 64-row tile of
+// them must span less than 2^31 bytes (kernels address tiles with 32-bit
+// byte offsets).
 int check_rows_aligned(const attn_tensor* t) {
   const int es = elem_size(t->dtype);
   const int64_t per16 = 16 / es;
   if (reinterpret_cast<uintptr_t>(t->data) % 16 != 0) return ATTN_ERR_STRIDE;
   if (t->stride[0] % per16 != 0 || t->stride[1] % per16 != 0) return ATTN_ERR_STRIDE;
+  if (t->shape[0] > 1 && t->stride[0] < t->shape[2]) return ATTN_ERR_STRIDE;
+  if (t->stride[0] * es * 64 >= ((int64_t)1 << 31)) return ATTN_ERR_RANGE;
   return ATTN_OK;
 }
 

@@ -39,12 +39,15 @@ __global__ __launch_bounds__(256) void blocksel_fwd_bf16(const Params p) {
   __shared__ __attribute__((aligned(16))) bf16 Vs[BS * VS];
   __shared__ uint32_t qbits[BS][MAXW];
   __shared__ uint32_t ubits[MAXW];
+  __shared__ int blist[32 * MAXW];
+  __shared__ int nblist;
 
   const int b = xcd_remap(blockIdx.x, gridDim.x);
   const int tile = b % p.num_tiles;
   const int kvh = b / p.num_tiles;
   const int hidx = kvh / (p.Hkv / p.Hidx);
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   const int col = lane & 15, grp = lane >> 4;
   const int q0 = tile * BS;
   const int qlast = min(q0 + BS - 1, p.T - 1);
@@ -88,13 +91,35 @@ __global__ __launch_bounds__(256) void blocksel_fwd_bf16(const Params p) {
     for (int n = 0; n < NDV; ++n) acc[nb][n] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
 
+  // K/V staging: each thread owns NLD 16-byte chunks of a block's K and of
+  // its V; the next selected block is prefetched into registers while the
+  // current one is being used.
   constexpr int CH = D / 8;  // 16-byte chunks per row
+  constexpr int NLD = BS * CH / 256;
+  static_assert(BS * CH % 256 == 0, "whole chunks per thread");
+  bf16x8 kr[NLD], vr[NLD];
+  auto load_block = [&](int blk) {
+#pragma unroll
+    for (int u = 0; u < NLD; ++u) {
+      const int t = tid + 256 * u;
+      const int r = t / CH, c = t - r * CH;
+      const int j = blk * BS + r;
+      const bool ok = j < p.T;
+      const int jc = ok ? j : p.T - 1;
+      const bf16x8 kx = *reinterpret_cast<const bf16x8*>(kg + (int64_t)jc * p.k_row + (int64_t)kvh * p.k_head + 8 * c);
+      const bf16x8 vx = *reinterpret_cast<const bf16x8*>(vg + (int64_t)jc * p.v_row + (int64_t)kvh * p.v_head + 8 * c);
+      kr[u] = ok ? kx : bf16x8{};
+      vr[u] = ok ? vx : bf16x8{};
+    }
+  };
+
   // Passes over windows of 32*MAXW candidate blocks (one window covers
   // documents up to 32*MAXW*64 tokens before the query block).
   for (int wb = blo >> 5; wb <= (bhi >> 5); wb += MAXW) {
     const int nwords = min(MAXW, (bhi >> 5) - wb + 1);
-    // ---- selection bits of the 64 queries, 32 blocks per word
-    __syncthreads();  // previous pass finished with qbits / ubits / K / V
+    // ---- selection bits of the 64 queries, 32 blocks per word; the 32 byte
+    // loads of a word are independent (clamped index, masked bit)
+    __syncthreads();  // the previous pass is done with qbits / blist / K / V
     for (int t = tid; t < BS * nwords; t += 256) {
       const int q = t / nwords, w = t - q * nwords;
       uint32_t bits = 0;
@@ -102,98 +127,108 @@ __global__ __launch_bounds__(256) void blocksel_fwd_bf16(const Params p) {
       if (qrow_idx <= qlast) {
         const uint8_t* row = tab + (int64_t)qrow_idx * p.bsel_q;
         const int blk0 = 32 * (wb + w);
+#pragma unroll
         for (int u = 0; u < 32; ++u) {
           const int blk = blk0 + u;
-          if (blk >= blo && blk <= bhi && row[blk]) bits |= 1u << u;
+          const uint8_t v = row[min(max(blk, blo), bhi)];
+          bits |= (uint32_t)(v != 0 && blk >= blo && blk <= bhi) << u;
         }
       }
       qbits[q][w] = bits;
     }
     __syncthreads();
-    for (int w = tid; w < nwords; w += 256) {
+    // union over the 64 queries, then the list of blocks to stage
+    if (tid < nwords) {
       uint32_t u = 0;
-      for (int q = 0; q < BS; ++q) u |= qbits[q][w];
-      ubits[w] = u;
+      for (int q = 0; q < BS; ++q) u |= qbits[q][tid];
+      ubits[tid] = u;
     }
-    for (int w = 0; w < nwords; ++w) {
-      __syncthreads();  // ubits ready / previous block consumed
-      uint32_t pending = ubits[w];
-      while (pending) {
-        const int u = __builtin_ctz(pending);
-        pending &= pending - 1;
-        const int blk = 32 * (wb + w) + u;
-        const int kb0 = blk * BS;
-        for (int t = tid; t < BS * CH; t += 256) {
-          const int r = t / CH, c = t - r * CH;
-          const int j = kb0 + r;
-          bf16x8 kx = {}, vx = {};
-          if (j < p.T) {
-            kx = *reinterpret_cast<const bf16x8*>(kg + (int64_t)j * p.k_row + (int64_t)kvh * p.k_head + 8 * c);
-            vx = *reinterpret_cast<const bf16x8*>(vg + (int64_t)j * p.v_row + (int64_t)kvh * p.v_head + 8 * c);
-          }
-          *reinterpret_cast<bf16x8*>(&Ks[r * KS + 8 * c]) = kx;
-          *reinterpret_cast<bf16x8*>(&Vs[r * VS + 8 * c]) = vx;
+    __syncthreads();
+    if (tid == 0) {
+      int n = 0;
+      for (int w = 0; w < nwords; ++w) {
+        uint32_t pending = ubits[w];
+        while (pending) {
+          blist[n++] = 32 * (wb + w) + __builtin_ctz(pending);
+          pending &= pending - 1;
         }
-        __syncthreads();
+      }
+      nblist = n;
+    }
+    __syncthreads();
+    const int nbl = nblist;
+    if (nbl > 0) load_block(blist[0]);
+    for (int bi = 0; bi < nbl; ++bi) {
+      const int blk = blist[bi];
+      const int kb0 = blk * BS;
+      const int wsel = (blk >> 5) - wb, bsel_bit = blk & 31;
+      __syncthreads();  // the previous block has been consumed
+#pragma unroll
+      for (int u = 0; u < NLD; ++u) {
+        const int t = tid + 256 * u;
+        const int r = t / CH, c = t - r * CH;
+        *reinterpret_cast<bf16x8*>(&Ks[r * KS + 8 * c]) = kr[u];
+        *reinterpret_cast<bf16x8*>(&Vs[r * VS + 8 * c]) = vr[u];
+      }
+      __syncthreads();
+      if (bi + 1 < nbl) load_block(blist[bi + 1]);
 
-  #pragma unroll
-        for (int nb = 0; nb < NB_PER_WAVE; ++nb) {
-          const int ql = 16 * wave + 4 * nb + (col >> 2);
-          const bool sel = (qbits[ql][w] >> u) & 1u;
-          if (__ballot(sel) == 0) continue;  // none of the 4 queries picked this block
+#pragma unroll
+      for (int nb = 0; nb < NB_PER_WAVE; ++nb) {
+        const int ql = 16 * wave + 4 * nb + (col >> 2);
+        const bool sel = (qbits[ql][wsel] >> bsel_bit) & 1u;
+        if (__ballot(sel) == 0) continue;  // none of the 4 queries picked this block
 
-          float s[4][4];
-  #pragma unroll
-          for (int sb = 0; sb < 4; ++sb) {
-            floatx4 a = {0.f, 0.f, 0.f, 0.f};
-            const bf16* krow = &Ks[(16 * sb + col) * KS + 8 * grp];
-  #pragma unroll
-            for (int c = 0; c < NQC; ++c)
-              a = mfma32(*reinterpret_cast<const bf16x8*>(krow + 32 * c), qf[nb][c], a);
-  #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int j = kb0 + 16 * sb + 4 * grp + e;
-              float x = a[e] * sl2;
-              if (SINK == kSinkKey0 && j == dstart[nb]) x += bias2;
-              s[sb][e] = (sel && j <= qi[nb] && j >= dstart[nb]) ? x : kNegInf;
-            }
-          }
-          float mt = kNegInf;
-  #pragma unroll
-          for (int sb = 0; sb < 4; ++sb)
-  #pragma unroll
-            for (int e = 0; e < 4; ++e) mt = fmaxf(mt, s[sb][e]);
-          mt = max_over_groups(mt);
-          const float mn = fmaxf(m2[nb], mt);
-          const float mu = (mn == kNegInf) ? 0.0f : mn;
-          const float alpha = exp2f_fast(m2[nb] - mu);
-          float ps = 0.0f;
-  #pragma unroll
-          for (int sb = 0; sb < 4; ++sb)
-  #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              s[sb][e] = exp2f_fast(s[sb][e] - mu);
-              ps += s[sb][e];
-            }
-          lsum[nb] = lsum[nb] * alpha + ps;
-          m2[nb] = mn;
-  #pragma unroll
-          for (int c2 = 0; c2 < 2; ++c2) {
-            bf16x8 pb;
-  #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              pb[e] = static_cast<bf16>(s[2 * c2][e]);
-              pb[4 + e] = static_cast<bf16>(s[2 * c2 + 1][e]);
-            }
-            const bf16* v0 = &Vs[(32 * c2 + 4 * grp + (col >> 2)) * VS + 4 * (col & 3)];
-  #pragma unroll
-            for (int n = 0; n < NDV; ++n) {
-              const bf16x8 va = cat8(lds_read_tr4(v0 + 16 * n), lds_read_tr4(v0 + 16 * VS + 16 * n));
-              acc[nb][n] = mfma32(va, pb, c2 == 0 ? acc[nb][n] * alpha : acc[nb][n]);
-            }
+        float s[4][4];
+#pragma unroll
+        for (int sb = 0; sb < 4; ++sb) {
+          floatx4 a = {0.f, 0.f, 0.f, 0.f};
+          const bf16* krow = &Ks[(16 * sb + col) * KS + 8 * grp];
+#pragma unroll
+          for (int c = 0; c < NQC; ++c)
+            a = mfma32(*reinterpret_cast<const bf16x8*>(krow + 32 * c), qf[nb][c], a);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int j = kb0 + 16 * sb + 4 * grp + e;
+            float x = a[e] * sl2;
+            if (SINK == kSinkKey0) x += (j == dstart[nb]) ? bias2 : 0.0f;
+            s[sb][e] = (sel & (j <= qi[nb]) & (j >= dstart[nb])) ? x : kNegInf;
           }
         }
-        __syncthreads();  // K/V block consumed
+        float mt = kNegInf;
+#pragma unroll
+        for (int sb = 0; sb < 4; ++sb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) mt = fmaxf(mt, s[sb][e]);
+        mt = max_over_groups(mt);
+        const float mn = fmaxf(m2[nb], mt);
+        const float mu = (mn == kNegInf) ? 0.0f : mn;
+        const float alpha = exp2f_fast(m2[nb] - mu);
+        float ps = 0.0f;
+#pragma unroll
+        for (int sb = 0; sb < 4; ++sb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            s[sb][e] = exp2f_fast(s[sb][e] - mu);
+            ps += s[sb][e];
+          }
+        lsum[nb] = lsum[nb] * alpha + ps;
+        m2[nb] = mn;
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2) {
+          bf16x8 pb;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            pb[e] = static_cast<bf16>(s[2 * c2][e]);
+            pb[4 + e] = static_cast<bf16>(s[2 * c2 + 1][e]);
+          }
+          const bf16* v0 = &Vs[(32 * c2 + 4 * grp + (col >> 2)) * VS + 4 * (col & 3)];
+#pragma unroll
+          for (int n = 0; n < NDV; ++n) {
+            const bf16x8 va = cat8(lds_read_tr4(v0 + 16 * n), lds_read_tr4(v0 + 16 * VS + 16 * n));
+            acc[nb][n] = mfma32(va, pb, c2 == 0 ? acc[nb][n] * alpha : acc[nb][n]);
+          }
+        }
       }
     }
   }

@@ -74,6 +74,80 @@ __device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b) {
 
 __device__ __forceinline__ float exp2f_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Range-checked buffer loads: a buffer resource covers `nbytes` from `base`;
+// a load whose byte offset lies past the range returns zeros.  Tiles are
+// staged with one resource per tile (base = the tile's first row), so tails
+// past the last valid row come back as zeros without any per-lane select or
+// clamped address, and the per-lane offsets are loop invariant.
+constexpr int kBufferFlags = 0x00020000;  // dword3 of a raw (untyped) buffer resource
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, nbytes, kBufferFlags);
+}
+__device__ __forceinline__ bf16x8 buf_load16(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+// Direct-to-LDS 16-byte loads (global_load_lds_dwordx4): lane l of the wave
+// deposits its 16 bytes at lds + 16*l, so one wave instruction fills 1 KB of
+// LDS contiguously; `lds` must be the same for the whole wave.  The data
+// never passes through VGPRs, so several tiles can be in flight at once.
+__device__ __forceinline__ void load_lds16(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                   (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+// The same load, issued through inline assembly with an explicit M0 so that
+// the compiler's own LDS-DMA tracking (which cannot always tell which LDS
+// array an in-flight load targets, and then drains every load before any LDS
+// read) stays out of the way: callers wait with wait_vmcnt before reading the
+// destination.  `lds_addr` is the wave-uniform byte address in LDS.  M0 is
+// written here; none of the kernels keep a value in M0 across these loads.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void load_lds16_m0(const void* g, uint32_t lds_byte_addr) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(lds_byte_addr), "v"(g) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Wait until at most N vector-memory operations of this wave are in flight
+// (gfx9 s_waitcnt: vmcnt in bits [3:0] and [15:14]; expcnt / lgkmcnt left at
+// their maxima, i.e. not waited on).  Vector loads complete in issue order.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// Workgroup barrier for hand-offs through LDS only: this wave's LDS accesses
+// have completed (lgkmcnt(0)) and every wave has arrived.  Unlike
+// __syncthreads it does not drain outstanding global loads (vmcnt), so
+// direct-to-LDS loads issued for later tiles stay in flight across it; the
+// loads a tile depends on are waited for explicitly with wait_vmcnt.  The
+// empty asm statements keep the compiler from moving memory accesses across.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt, expcnt not waited
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// 16-byte-chunk swizzle for row-major LDS tiles whose rows are a multiple of
+// 128 bytes long: chunk c of row r is stored at chunk c ^ swz16(r).  Eight
+// consecutive rows then put a given chunk in eight different bank groups
+// (16-byte MFMA operand reads), and four consecutive rows starting at a
+// multiple of 4 put a 32-byte column pair in four different bank groups
+// (transposing reads).
+__device__ __forceinline__ int swz16(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+
+// Lazy rescaling: the running reference max only moves when a new logit
+// exceeds it by more than this (log2 units), so exp2(s - m) stays <= 2^8 and
+// the accumulator rescale (a pass over every accumulator register) is skipped
+// on almost every tile.  Exact: any reference works as long as the terms stay
+// in range; the final normalisation uses the same reference.
+constexpr float kRescaleLog2 = 8.0f;
+
 // max / sum over the four 16-lane groups holding the same MFMA column
 __device__ __forceinline__ float max_over_groups(float x) {
   x = fmaxf(x, __shfl_xor(x, 16));

@@ -8,10 +8,14 @@
 // outside [0, Tk)) as padding anywhere in a row.
 //
 // One workgroup = one query row x 64 heads (4 waves x 16 heads); the row's
-// index list is shared by all 64 heads, so each gathered 1152-byte KV row is
-// staged once in LDS and used by every head.  The row's list is first
+// index list is shared by all 64 heads, so each gathered 1152-byte latent row
+// is staged once in LDS and used by every head.  The row's list is first
 // compacted in LDS (a workgroup prefix sum over the valid entries), so padding
-// costs one pass over the list and no key tiles.  Per 32-key tile and wave:
+// costs one pass over the list and no key tiles.  Key tiles of 32 gathered
+// rows go straight from memory into a 3-stage LDS ring (direct-to-LDS loads,
+// two tiles in flight behind the one being computed, waited for explicitly),
+// stored with a 16-byte chunk swizzle so both operand reads below are free of
+// bank conflicts.  Per tile and wave:
 //   S^T[key][head] = K[key][:576] . Q[head][:576]   (18 MFMA 16x16x32 per 16 keys;
 //                                                   Q of the wave's 16 heads in VGPRs)
 //   O^T[dv][head] += V^T[dv][key] . P^T[key][head]  (32 MFMAs; V^T read from the
@@ -27,17 +31,24 @@ namespace mla {
 constexpr int DQK = 576, DV = 512;
 constexpr int HPW = 16, NW = 4, HPB = HPW * NW;   // heads per wave / per workgroup
 constexpr int KT = 32;                           // keys per LDS tile
-constexpr int KS = DQK + 8;                      // LDS row stride (elements)
+constexpr int RCH = DQK / 8;                     // 72 16-byte chunks per latent row
+constexpr int TILE_CH = KT * RCH;                // 2304 chunks = 36 KB per tile
+constexpr int TILE_EL = TILE_CH * 8;             // bf16 elements per tile
+constexpr int NSTAGE = 3;                        // LDS ring depth
+constexpr int LDPW = TILE_CH / 64 / NW;          // 9 direct-to-LDS loads per wave per tile
 constexpr int CHUNK = 2048;                      // list entries compacted per pass
 constexpr int NQC = DQK / 32;                    // 18 Q^T fragments
 constexpr int NDV = DV / 16;                     // 32 output blocks
-constexpr int RCH = DQK / 8;                     // 72 16-byte chunks per KV row
+constexpr int KPIPE = 4;                         // K operand reads kept in flight
+static_assert(TILE_CH % (64 * NW) == 0, "whole wave loads per tile");
 }  // namespace mla
 
 template <int SINK>
 __global__ __launch_bounds__(256) void topk_mla_fwd_bf16(const Params p) {
   using namespace mla;
-  __shared__ __attribute__((aligned(16))) bf16 Ks[KT * KS];
+  __shared__ __attribute__((aligned(16))) bf16 ks0[TILE_EL];
+  __shared__ __attribute__((aligned(16))) bf16 ks1[TILE_EL];
+  __shared__ __attribute__((aligned(16))) bf16 ks2[TILE_EL];
   __shared__ int kidx[CHUNK];
   __shared__ int wsum[NW];
 
@@ -45,7 +56,8 @@ __global__ __launch_bounds__(256) void topk_mla_fwd_bf16(const Params p) {
   const int b = blockIdx.x;
   const int i = b / ngroups;
   const int hg = b - i * ngroups;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   const int col = lane & 15, grp = lane >> 4;
   const int h = hg * HPB + wave * HPW + col;  // this lane's head
 
@@ -58,6 +70,18 @@ __global__ __launch_bounds__(256) void topk_mla_fwd_bf16(const Params p) {
     for (int c = 0; c < NQC; ++c) qf[c] = *reinterpret_cast<const bf16x8*>(qrow + 32 * c);
   }
 
+  // Per-lane LDS element offsets within a tile (see swz16): K operand rows
+  // 16*sb + col, 16-byte chunks 4*cc + grp; V^T rows 4*grp + col/4 (+16),
+  // chunk pairs 2n, 2n+1.
+  const int kfr = swz16(col);
+  const int k_even = col * DQK + 8 * (grp ^ kfr);
+  const int k_odd = col * DQK + 8 * ((4 + grp) ^ kfr);
+  const int vfr = ((col >> 2) << 1) | (grp & 1);
+  const int vrow = (4 * grp + (col >> 2)) * DQK + 4 * (col & 1);
+  int voff[4];
+#pragma unroll
+  for (int n4 = 0; n4 < 4; ++n4) voff[n4] = vrow + 8 * ((2 * n4 + ((col >> 1) & 1)) ^ vfr);
+
   const float sl2 = p.scale_log2;
   float m2 = kNegInf, lsum = 0.0f;
   floatx4 acc[NDV];
@@ -67,7 +91,7 @@ __global__ __launch_bounds__(256) void topk_mla_fwd_bf16(const Params p) {
   const int32_t* idx_row = p.topk_idx + (int64_t)i * p.topk_row;
   for (int c0 = 0; c0 < p.topk; c0 += CHUNK) {
     // ---- compact the valid entries of list[c0, c0 + CHUNK) into kidx[]
-    __syncthreads();  // kidx / Ks of the previous pass are consumed
+    __syncthreads();  // kidx / the LDS ring of the previous pass are consumed
     int mine[CHUNK / 256];
     int cnt = 0;
 #pragma unroll
@@ -98,28 +122,46 @@ __global__ __launch_bounds__(256) void topk_mla_fwd_bf16(const Params p) {
       if (mine[u] >= 0) kidx[pos++] = mine[u];
     __syncthreads();
 
-    // ---- key tiles over the compacted list
-    for (int t0 = 0; t0 < nvalid; t0 += KT) {
-      for (int f = tid; f < KT * RCH; f += 256) {
-        const int r = f / RCH, c = f - r * RCH;
-        bf16x8 v = {};
-        if (t0 + r < nvalid)
-          v = *reinterpret_cast<const bf16x8*>(kg + (int64_t)kidx[t0 + r] * p.k_row + 8 * c);
-        *reinterpret_cast<bf16x8*>(&Ks[r * KS + 8 * c]) = v;
+    // ---- gather tile t into a stage: this wave's LDPW 1-KB pieces.  Rows
+    // past the valid count re-read a valid row (finite data; their logits are
+    // masked to -inf, so they carry zero weight).
+    const int ntiles = (nvalid + KT - 1) / KT;
+    auto issue = [&](int t, bf16* st) {
+      const uint32_t st_addr = lds_addr(st) + (uint32_t)(wave * LDPW * 1024);
+#pragma unroll
+      for (int u = 0; u < LDPW; ++u) {
+        const int ch = (wave * LDPW + u) * 64 + lane;
+        const int r = ch / RCH, cc = ch - r * RCH;
+        const int posr = t * KT + r;
+        const int j = kidx[posr < nvalid ? posr : 0];
+        load_lds16_m0(kg + (int64_t)j * p.k_row + 8 * (cc ^ swz16(r)), st_addr + u * 1024);
       }
-      __syncthreads();
+    };
 
+    // ---- one tile: S, online softmax with lazy rescale, PV
+    auto compute = [&](int t, const bf16* st) {
+      const int t0 = t * KT;
       float s[2][4];
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb) {
         floatx4 a = {0.f, 0.f, 0.f, 0.f};
-        const bf16* krow = &Ks[(16 * sb + col) * KS + 8 * grp];
+        const bf16* krow = st + sb * 16 * DQK;
+        bf16x8 kb[KPIPE];
 #pragma unroll
-        for (int c = 0; c < NQC; ++c)
-          a = mfma32(*reinterpret_cast<const bf16x8*>(krow + 32 * c), qf[c], a);
+        for (int cc = 0; cc < KPIPE; ++cc)
+          kb[cc] = *reinterpret_cast<const bf16x8*>(krow + 64 * (cc >> 1) + ((cc & 1) ? k_odd : k_even));
+#pragma unroll
+        for (int cc = 0; cc < NQC; ++cc) {
+          a = mfma32(kb[cc % KPIPE], qf[cc], a);
+          const int nx = cc + KPIPE;
+          if (nx < NQC)
+            kb[cc % KPIPE] =
+                *reinterpret_cast<const bf16x8*>(krow + 64 * (nx >> 1) + ((nx & 1) ? k_odd : k_even));
+        }
+        const bool all_in = t0 + 16 * sb + 4 * grp + 3 < nvalid;
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          s[sb][e] = (t0 + 16 * sb + 4 * grp + e < nvalid) ? a[e] * sl2 : kNegInf;
+          s[sb][e] = (all_in | (t0 + 16 * sb + 4 * grp + e < nvalid)) ? a[e] * sl2 : kNegInf;
       }
       float mt = kNegInf;
 #pragma unroll
@@ -127,9 +169,15 @@ __global__ __launch_bounds__(256) void topk_mla_fwd_bf16(const Params p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) mt = fmaxf(mt, s[sb][e]);
       mt = max_over_groups(mt);
-      const float mn = fmaxf(m2, mt);
-      const float mu = (mn == kNegInf) ? 0.0f : mn;
-      const float alpha = exp2f_fast(m2 - mu);
+      if (__ballot(mt > m2 + kRescaleLog2) != 0) {  // lazy rescale (wave-uniform)
+        const float mn = fmaxf(m2, mt);
+        const float alpha = (m2 == mn) ? 1.0f : exp2f_fast(m2 - mn);
+        lsum *= alpha;
+#pragma unroll
+        for (int n = 0; n < NDV; ++n) acc[n] *= alpha;
+        m2 = mn;
+      }
+      const float mu = (m2 == kNegInf) ? 0.0f : m2;
       float ps = 0.0f;
       bf16x8 pb;
 #pragma unroll
@@ -140,15 +188,29 @@ __global__ __launch_bounds__(256) void topk_mla_fwd_bf16(const Params p) {
           ps += pe;
           pb[4 * sb + e] = static_cast<bf16>(pe);
         }
-      lsum = lsum * alpha + ps;
-      m2 = mn;
-      const bf16* v0 = &Ks[(4 * grp + (col >> 2)) * KS + 4 * (col & 3)];
+      lsum += ps;
 #pragma unroll
       for (int n = 0; n < NDV; ++n) {
-        const bf16x8 va = cat8(lds_read_tr4(v0 + 16 * n), lds_read_tr4(v0 + 16 * KS + 16 * n));
-        acc[n] = mfma32(va, pb, acc[n] * alpha);
+        const bf16* v0 = st + 64 * (n >> 2) + voff[n & 3];
+        const bf16x8 va = cat8(lds_read_tr4(v0), lds_read_tr4(v0 + 16 * DQK));
+        acc[n] = mfma32(va, pb, acc[n]);
       }
-      __syncthreads();  // Ks consumed before the next tile is staged
+    };
+
+    // tile t lives in stage t % 3; the loop is unrolled by the ring depth so
+    // every LDS access names its stage array at compile time
+    auto step = [&](int t, bf16* cur, bf16* ahead2) {
+      if (t + 1 < ntiles) wait_vmcnt<LDPW>(); else wait_vmcnt<0>();
+      lds_barrier();  // tile t is in LDS for every wave; tile t-1's stage is free
+      if (t + 2 < ntiles) issue(t + 2, ahead2);
+      compute(t, cur);
+    };
+    if (ntiles > 0) issue(0, ks0);
+    if (ntiles > 1) issue(1, ks1);
+    for (int t = 0; t < ntiles; t += NSTAGE) {
+      step(t, ks0, ks2);
+      if (t + 1 < ntiles) step(t + 1, ks1, ks0);
+      if (t + 2 < ntiles) step(t + 2, ks2, ks1);
     }
   }
 

@@ -31,10 +31,14 @@ struct WinCfg {
   // rows and the 4-row transposing V reads each hit distinct LDS banks.
   static constexpr int KS = D + 8;
   static constexpr int VS = (((D / 2) % 32) == 8 || ((D / 2) % 32) == 24) ? D : D + 16;
+  // Waves per SIMD the register budget is held to: 4 resident workgroups per
+  // CU keep 4 x 64 rows of one tile in flight for the small head dims.
+  static constexpr int WAVES = D <= 96 ? 4 : 3;
 };
 
 template <int D, int SINK>
-__global__ __launch_bounds__(256) void window_fwd_bf16(const Params p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WinCfg<D>::WAVES, WinCfg<D>::WAVES)))
+void window_fwd_bf16(const Params p) {
   using C = WinCfg<D>;
   static_assert(D % 16 == 0 && D <= 256, "head dim");
   __shared__ __attribute__((aligned(16))) bf16 Ks[C::KT * C::KS];
@@ -44,7 +48,8 @@ __global__ __launch_bounds__(256) void window_fwd_bf16(const Params p) {
   const int tile = b % p.num_tiles;
   const int h = b / p.num_tiles;
   const int kvh = h / p.group;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   const int col = lane & 15, grp = lane >> 4;
   const int r0 = tile * C::BM;
   const int rlast = min(r0 + C::BM - 1, p.T - 1);
@@ -64,12 +69,15 @@ __global__ __launch_bounds__(256) void window_fwd_bf16(const Params p) {
   int kmin, kmax, tmp;
   row_window(r0, kmin, tmp, tmp);
   row_window(rlast, tmp, kmax, tmp);
-  int wlo = 0x7fffffff, whi = -1;  // this wave's band
+  // This wave's band [wlo, whi]; its interior [lo of the last row, hi of the
+  // first row] is valid for every row of the wave, so sub-blocks inside it
+  // need no per-element mask; key-0 positions of the wave lie in [k0a, k0b].
+  int wlo = 0x7fffffff, whi = -1, ilo = 0x7fffffff, ihi = -1, k0a = -1, k0b = -1;
   {
     const int wr0 = r0 + wave * 16;
     if (wr0 <= rlast) {
-      row_window(wr0, wlo, tmp, tmp);
-      row_window(min(wr0 + 15, rlast), tmp, whi, tmp);
+      row_window(wr0, wlo, ihi, k0a);
+      row_window(min(wr0 + 15, rlast), ilo, whi, k0b);
     }
   }
 
@@ -99,21 +107,53 @@ __global__ __launch_bounds__(256) void window_fwd_bf16(const Params p) {
 #pragma unroll
   for (int n = 0; n < C::NDV; ++n) acc[n] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  constexpr int CH = D / 8;  // 16-byte chunks per row
+  // K/V staging: every thread owns NLD 16-byte chunks of each tile, fetched
+  // with range-checked buffer loads (rows past the band come back as zeros).
+  // The next tile's loads are issued right after the current tile is written
+  // to LDS, so their latency overlaps this tile's MFMA work.
+  constexpr int CH = D / 8;                          // 16-byte chunks per row
+  constexpr int NLD = (C::KT * CH + 255) / 256;
+  const bf16* kh = kg + (int64_t)kvh * p.k_head;
+  const bf16* vh = vg + (int64_t)kvh * p.v_head;
+  int koff[NLD], voff[NLD];
+#pragma unroll
+  for (int u = 0; u < NLD; ++u) {
+    const int t = tid + 256 * u;
+    const int r = t / CH, c = t - r * CH;
+    koff[u] = (int)((r * p.k_row + 8 * c) * 2);
+    voff[u] = (int)((r * p.v_row + 8 * c) * 2);
+  }
+  bf16x8 kr[NLD], vr[NLD];
+  auto load_tile = [&](int kt0) {
+    const int rows = min(C::KT, kmax - kt0 + 1);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kh + (int64_t)kt0 * p.k_row, (int)(rows * p.k_row * 2));
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vh + (int64_t)kt0 * p.v_row, (int)(rows * p.v_row * 2));
+#pragma unroll
+    for (int u = 0; u < NLD; ++u) {
+      if (tid + 256 * u < C::KT * CH) {
+        kr[u] = buf_load16(rk, koff[u]);
+        vr[u] = buf_load16(rv, voff[u]);
+      }
+    }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int u = 0; u < NLD; ++u) {
+      const int t = tid + 256 * u;
+      if (t < C::KT * CH) {
+        const int r = t / CH, c = t - r * CH;
+        *reinterpret_cast<bf16x8*>(&Ks[r * C::KS + 8 * c]) = kr[u];
+        *reinterpret_cast<bf16x8*>(&Vs[r * C::VS + 8 * c]) = vr[u];
+      }
+    }
+  };
+
+  load_tile(kmin);
   for (int kt0 = kmin; kt0 <= kmax; kt0 += C::KT) {
     __syncthreads();  // the previous tile has been consumed
-    for (int t = tid; t < C::KT * CH; t += 256) {
-      const int r = t / CH, c = t - r * CH;
-      const int j = kt0 + r;
-      bf16x8 kx = {}, vx = {};
-      if (j <= kmax) {
-        kx = *reinterpret_cast<const bf16x8*>(kg + (int64_t)j * p.k_row + (int64_t)kvh * p.k_head + 8 * c);
-        vx = *reinterpret_cast<const bf16x8*>(vg + (int64_t)j * p.v_row + (int64_t)kvh * p.v_head + 8 * c);
-      }
-      *reinterpret_cast<bf16x8*>(&Ks[r * C::KS + 8 * c]) = kx;
-      *reinterpret_cast<bf16x8*>(&Vs[r * C::VS + 8 * c]) = vx;
-    }
+    store_tile();
     __syncthreads();
+    if (kt0 + C::KT <= kmax) load_tile(kt0 + C::KT);
     if (kt0 > whi || kt0 + C::KT - 1 < wlo) continue;  // wave-uniform
 
     float s[4][4];
@@ -134,12 +174,16 @@ __global__ __launch_bounds__(256) void window_fwd_bf16(const Params p) {
         a = mfma32(*reinterpret_cast<const bf16x8*>(krow + 32 * c + 8 * grp), qf[c], a);
       if (C::TAIL16)
         a = mfma16(*reinterpret_cast<const bf16x4*>(krow + 32 * C::NC32 + 4 * grp), qt, a);
+      const bool interior = kb0 >= ilo && kb0 + 15 <= ihi;          // wave-uniform
+      const bool has_key0 = SINK == kSinkKey0 && kb0 <= k0b && kb0 + 15 >= k0a;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int j = kb0 + 4 * grp + e;
         float x = a[e] * sl2;
-        if (SINK == kSinkKey0 && j == key0) x += bias2;
-        s[sb][e] = (j >= lo && j <= hi) ? x : kNegInf;
+        // bitwise (not short-circuit) logic: one select per element, no
+        // divergent branches between the MFMA and the read of its result
+        if (SINK == kSinkKey0) x += (has_key0 & (j == key0)) ? bias2 : 0.0f;
+        s[sb][e] = (interior | ((j >= lo) & (j <= hi))) ? x : kNegInf;
       }
     }
 
@@ -163,8 +207,10 @@ __global__ __launch_bounds__(256) void window_fwd_bf16(const Params p) {
       }
     lsum = lsum * alpha + ps;
     m2 = mn;
+    if (__ballot(alpha != 1.0f) != 0) {  // skip the rescale when no row's max moved
 #pragma unroll
-    for (int n = 0; n < C::NDV; ++n) acc[n] *= alpha;
+      for (int n = 0; n < C::NDV; ++n) acc[n] *= alpha;
+    }
 
 #pragma unroll
     for (int c2 = 0; c2 < 2; ++c2) {
