@@ -8,12 +8,15 @@
 // its 4 query heads.  The selection rows of the 64 queries are packed into
 // per-query bit masks in LDS (64-bit table offsets), and their union decides
 // which key blocks are staged at all: each selected block is loaded once into
-// LDS (K and V row-major, coalesced) and shared by all 64 queries x 4 heads.
-// MFMA columns are (query, head) pairs: a 16-column block holds 4 queries x
-// their 4 heads, so the 4 heads of a query -- which share one selection --
-// fill the MFMA's N dimension.  Per 16-column block the wave skips a staged
-// key block unless one of its 4 queries selected it (wave-uniform ballot), so
-// MFMA work follows the union of 4 queries' selections, not of 64.
+// LDS and shared by all 64 queries x 4 heads.  Blocks go straight from memory
+// into a 3-stage LDS ring (direct-to-LDS loads; two blocks in flight behind
+// the one being computed), K and V row-major with a 16-byte chunk swizzle so
+// the operand reads are free of bank conflicts.  MFMA columns are
+// (query, head) pairs: a 16-column block holds 4 queries x their 4 heads, so
+// the 4 heads of a query -- which share one selection -- fill the MFMA's N
+// dimension.  Per 16-column block the wave skips a staged key block unless one
+// of its 4 queries selected it (wave-uniform ballot), so MFMA work follows the
+// union of 4 queries' selections, not of 64.
 //   S^T[key][(q,h)] = K[key][:] . Q[(q,h)][:]      (MFMA 16x16x32 bf16, Q in VGPRs)
 //   O^T[dv][(q,h)] += V^T[dv][key] . P^T[key][(q,h)]
 #include "common.hpp"
@@ -22,21 +25,24 @@ namespace attn {
 
 namespace bsel {
 constexpr int D = 128;
-constexpr int G = 4;          // query heads per kv head
-constexpr int BS = 64;        // key block size = query tile
+constexpr int G = 4;            // query heads per kv head
+constexpr int BS = 64;          // key block size = query tile
+constexpr int NW = 4;           // waves per workgroup
 constexpr int NB_PER_WAVE = 4;  // 16-column blocks per wave (16 queries x 4 heads)
-constexpr int NQC = D / 32;   // 4 Q^T fragments per column block
-constexpr int NDV = D / 16;   // 8 output blocks
-constexpr int KS = D + 8;     // K LDS row stride: 68 dwords
-constexpr int VS = D + 16;    // V LDS row stride: 72 dwords
-constexpr int MAXW = 32;      // selection words per query held in LDS per pass (1024 blocks)
+constexpr int NQC = D / 32;     // 4 Q^T fragments per column block
+constexpr int NDV = D / 16;     // 8 output blocks
+constexpr int RCH = D / 8;      // 16 16-byte chunks per row
+constexpr int TILE_EL = BS * D; // bf16 elements of one K (or V) block
+constexpr int LDPW = BS * RCH / 64 / NW;  // 4 direct-to-LDS loads per wave per tensor
+constexpr int MAXW = 32;        // selection words per query held in LDS per pass (1024 blocks)
 }  // namespace bsel
 
 template <int SINK>
 __global__ __launch_bounds__(256) void blocksel_fwd_bf16(const Params p) {
   using namespace bsel;
-  __shared__ __attribute__((aligned(16))) bf16 Ks[BS * KS];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[BS * VS];
+  __shared__ __attribute__((aligned(16))) bf16 kv0[2 * TILE_EL];  // stage = K block, V block
+  __shared__ __attribute__((aligned(16))) bf16 kv1[2 * TILE_EL];
+  __shared__ __attribute__((aligned(16))) bf16 kv2[2 * TILE_EL];
   __shared__ uint32_t qbits[BS][MAXW];
   __shared__ uint32_t ubits[MAXW];
   __shared__ int blist[32 * MAXW];
@@ -63,8 +69,8 @@ __global__ __launch_bounds__(256) void blocksel_fwd_bf16(const Params p) {
   const int hh = col & 3;
   const int h = kvh * G + hh;
   const bf16* qg = static_cast<const bf16*>(p.q);
-  const bf16* kg = static_cast<const bf16*>(p.k);
-  const bf16* vg = static_cast<const bf16*>(p.v);
+  const bf16* kg = static_cast<const bf16*>(p.k) + (int64_t)kvh * p.k_head;
+  const bf16* vg = static_cast<const bf16*>(p.v) + (int64_t)kvh * p.v_head;
   bf16x8 qf[NB_PER_WAVE][NQC];
 #pragma unroll
   for (int nb = 0; nb < NB_PER_WAVE; ++nb) {
@@ -79,6 +85,19 @@ __global__ __launch_bounds__(256) void blocksel_fwd_bf16(const Params p) {
     }
   }
 
+  // Per-lane LDS element offsets within a block (see swz16): K operand rows
+  // 16*sb + col, chunks 4*cc + grp; V^T rows 32*c2 + 4*grp + col/4 (+16),
+  // chunk pairs 2n, 2n+1.
+  const int kfr = swz16(col);
+  int koff[NQC];
+#pragma unroll
+  for (int cc = 0; cc < NQC; ++cc) koff[cc] = col * D + 8 * ((4 * cc + grp) ^ kfr);
+  const int vfr = ((col >> 2) << 1) | (grp & 1);
+  const int vrow = (4 * grp + (col >> 2)) * D + 4 * (col & 1);
+  int voff[NDV];
+#pragma unroll
+  for (int n = 0; n < NDV; ++n) voff[n] = vrow + 8 * ((2 * n + ((col >> 1) & 1)) ^ vfr);
+
   const float sl2 = p.scale_log2;
   const float bias2 = (SINK == kSinkKey0) ? __ldg(p.sinks + h) * kLog2e : 0.0f;
   float m2[NB_PER_WAVE], lsum[NB_PER_WAVE];
@@ -91,25 +110,93 @@ __global__ __launch_bounds__(256) void blocksel_fwd_bf16(const Params p) {
     for (int n = 0; n < NDV; ++n) acc[nb][n] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // K/V staging: each thread owns NLD 16-byte chunks of a block's K and of
-  // its V; the next selected block is prefetched into registers while the
-  // current one is being used.
-  constexpr int CH = D / 8;  // 16-byte chunks per row
-  constexpr int NLD = BS * CH / 256;
-  static_assert(BS * CH % 256 == 0, "whole chunks per thread");
-  bf16x8 kr[NLD], vr[NLD];
-  auto load_block = [&](int blk) {
+  // ---- stage one key block (K then V, this wave's LDPW 1-KB pieces of each);
+  // rows past T re-read row T-1 (finite data; masked by causality).
+  auto issue = [&](int blk, bf16* st) {
+    const uint32_t base = lds_addr(st) + (uint32_t)(wave * LDPW * 1024);
 #pragma unroll
-    for (int u = 0; u < NLD; ++u) {
-      const int t = tid + 256 * u;
-      const int r = t / CH, c = t - r * CH;
-      const int j = blk * BS + r;
-      const bool ok = j < p.T;
-      const int jc = ok ? j : p.T - 1;
-      const bf16x8 kx = *reinterpret_cast<const bf16x8*>(kg + (int64_t)jc * p.k_row + (int64_t)kvh * p.k_head + 8 * c);
-      const bf16x8 vx = *reinterpret_cast<const bf16x8*>(vg + (int64_t)jc * p.v_row + (int64_t)kvh * p.v_head + 8 * c);
-      kr[u] = ok ? kx : bf16x8{};
-      vr[u] = ok ? vx : bf16x8{};
+    for (int u = 0; u < LDPW; ++u) {
+      const int ch = (wave * LDPW + u) * 64 + lane;
+      const int r = ch / RCH, cc = ch - r * RCH;
+      const int j = min(blk * BS + r, p.T - 1);
+      const int c = 8 * (cc ^ swz16(r));
+      load_lds16_m0(kg + (int64_t)j * p.k_row + c, base + u * 1024);
+      load_lds16_m0(vg + (int64_t)j * p.v_row + c, base + TILE_EL * 2 + u * 1024);
+    }
+  };
+
+  // ---- one staged block for this wave's 4 column blocks
+  auto compute = [&](int blk, int wsel, const bf16* st) {
+    const int kb0 = blk * BS;
+    const bf16* ks = st;
+    const bf16* vs = st + TILE_EL;
+#pragma unroll
+    for (int nb = 0; nb < NB_PER_WAVE; ++nb) {
+      const int ql = 16 * wave + 4 * nb + (col >> 2);
+      const bool sel = (qbits[ql][wsel] >> (blk & 31)) & 1u;
+      if (__ballot(sel) == 0) continue;  // none of the 4 queries picked this block
+      // is the whole block causal and inside the document for every column?
+      const bool whole = (kb0 >= dstart[nb]) & (kb0 + BS - 1 <= qi[nb]);
+      const bool edge = __ballot(sel & !whole) != 0;
+      const bool has_key0 =
+          SINK == kSinkKey0 && __ballot(sel & (dstart[nb] >= kb0) & (dstart[nb] < kb0 + BS)) != 0;
+
+      float s[4][4];
+#pragma unroll
+      for (int sb = 0; sb < 4; ++sb) {
+        floatx4 a = {0.f, 0.f, 0.f, 0.f};
+        const bf16* krow = ks + sb * 16 * D;
+#pragma unroll
+        for (int cc = 0; cc < NQC; ++cc)
+          a = mfma32(*reinterpret_cast<const bf16x8*>(krow + koff[cc]), qf[nb][cc], a);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int j = kb0 + 16 * sb + 4 * grp + e;
+          float x = a[e] * sl2;
+          if (has_key0) x += (j == dstart[nb]) ? bias2 : 0.0f;
+          const bool ok = edge ? (sel & (j <= qi[nb]) & (j >= dstart[nb])) : sel;
+          s[sb][e] = ok ? x : kNegInf;
+        }
+      }
+      float mt = kNegInf;
+#pragma unroll
+      for (int sb = 0; sb < 4; ++sb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) mt = fmaxf(mt, s[sb][e]);
+      mt = max_over_groups(mt);
+      if (__ballot(mt > m2[nb] + kRescaleLog2) != 0) {  // lazy rescale (wave-uniform)
+        const float mn = fmaxf(m2[nb], mt);
+        const float alpha = (m2[nb] == mn) ? 1.0f : exp2f_fast(m2[nb] - mn);
+        lsum[nb] *= alpha;
+#pragma unroll
+        for (int n = 0; n < NDV; ++n) acc[nb][n] *= alpha;
+        m2[nb] = mn;
+      }
+      const float mu = (m2[nb] == kNegInf) ? 0.0f : m2[nb];
+      float ps = 0.0f;
+#pragma unroll
+      for (int sb = 0; sb < 4; ++sb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          s[sb][e] = exp2f_fast(s[sb][e] - mu);
+          ps += s[sb][e];
+        }
+      lsum[nb] += ps;
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) {
+        bf16x8 pb;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          pb[e] = static_cast<bf16>(s[2 * c2][e]);
+          pb[4 + e] = static_cast<bf16>(s[2 * c2 + 1][e]);
+        }
+        const bf16* v0 = vs + c2 * 32 * D;
+#pragma unroll
+        for (int n = 0; n < NDV; ++n) {
+          const bf16x8 va = cat8(lds_read_tr4(v0 + voff[n]), lds_read_tr4(v0 + 16 * D + voff[n]));
+          acc[nb][n] = mfma32(va, pb, acc[nb][n]);
+        }
+      }
     }
   };
 
@@ -119,7 +206,7 @@ __global__ __launch_bounds__(256) void blocksel_fwd_bf16(const Params p) {
     const int nwords = min(MAXW, (bhi >> 5) - wb + 1);
     // ---- selection bits of the 64 queries, 32 blocks per word; the 32 byte
     // loads of a word are independent (clamped index, masked bit)
-    __syncthreads();  // the previous pass is done with qbits / blist / K / V
+    __syncthreads();  // the previous pass is done with qbits / blist / the ring
     for (int t = tid; t < BS * nwords; t += 256) {
       const int q = t / nwords, w = t - q * nwords;
       uint32_t bits = 0;
@@ -131,7 +218,7 @@ __global__ __launch_bounds__(256) void blocksel_fwd_bf16(const Params p) {
         for (int u = 0; u < 32; ++u) {
           const int blk = blk0 + u;
           const uint8_t v = row[min(max(blk, blo), bhi)];
-          bits |= (uint32_t)(v != 0 && blk >= blo && blk <= bhi) << u;
+          bits |= (uint32_t)((v != 0) & (blk >= blo) & (blk <= bhi)) << u;
         }
       }
       qbits[q][w] = bits;
@@ -157,79 +244,22 @@ __global__ __launch_bounds__(256) void blocksel_fwd_bf16(const Params p) {
     }
     __syncthreads();
     const int nbl = nblist;
-    if (nbl > 0) load_block(blist[0]);
-    for (int bi = 0; bi < nbl; ++bi) {
+
+    // block bi lives in stage bi % 3; the loop is unrolled by the ring depth
+    // so every stage is a compile-time LDS array
+    auto step = [&](int bi, bf16* cur, bf16* ahead2) {
+      if (bi + 1 < nbl) wait_vmcnt<2 * LDPW>(); else wait_vmcnt<0>();
+      lds_barrier();  // block bi is in LDS for every wave; block bi-1's stage is free
+      if (bi + 2 < nbl) issue(blist[bi + 2], ahead2);
       const int blk = blist[bi];
-      const int kb0 = blk * BS;
-      const int wsel = (blk >> 5) - wb, bsel_bit = blk & 31;
-      __syncthreads();  // the previous block has been consumed
-#pragma unroll
-      for (int u = 0; u < NLD; ++u) {
-        const int t = tid + 256 * u;
-        const int r = t / CH, c = t - r * CH;
-        *reinterpret_cast<bf16x8*>(&Ks[r * KS + 8 * c]) = kr[u];
-        *reinterpret_cast<bf16x8*>(&Vs[r * VS + 8 * c]) = vr[u];
-      }
-      __syncthreads();
-      if (bi + 1 < nbl) load_block(blist[bi + 1]);
-
-#pragma unroll
-      for (int nb = 0; nb < NB_PER_WAVE; ++nb) {
-        const int ql = 16 * wave + 4 * nb + (col >> 2);
-        const bool sel = (qbits[ql][wsel] >> bsel_bit) & 1u;
-        if (__ballot(sel) == 0) continue;  // none of the 4 queries picked this block
-
-        float s[4][4];
-#pragma unroll
-        for (int sb = 0; sb < 4; ++sb) {
-          floatx4 a = {0.f, 0.f, 0.f, 0.f};
-          const bf16* krow = &Ks[(16 * sb + col) * KS + 8 * grp];
-#pragma unroll
-          for (int c = 0; c < NQC; ++c)
-            a = mfma32(*reinterpret_cast<const bf16x8*>(krow + 32 * c), qf[nb][c], a);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int j = kb0 + 16 * sb + 4 * grp + e;
-            float x = a[e] * sl2;
-            if (SINK == kSinkKey0) x += (j == dstart[nb]) ? bias2 : 0.0f;
-            s[sb][e] = (sel & (j <= qi[nb]) & (j >= dstart[nb])) ? x : kNegInf;
-          }
-        }
-        float mt = kNegInf;
-#pragma unroll
-        for (int sb = 0; sb < 4; ++sb)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) mt = fmaxf(mt, s[sb][e]);
-        mt = max_over_groups(mt);
-        const float mn = fmaxf(m2[nb], mt);
-        const float mu = (mn == kNegInf) ? 0.0f : mn;
-        const float alpha = exp2f_fast(m2[nb] - mu);
-        float ps = 0.0f;
-#pragma unroll
-        for (int sb = 0; sb < 4; ++sb)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            s[sb][e] = exp2f_fast(s[sb][e] - mu);
-            ps += s[sb][e];
-          }
-        lsum[nb] = lsum[nb] * alpha + ps;
-        m2[nb] = mn;
-#pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2) {
-          bf16x8 pb;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            pb[e] = static_cast<bf16>(s[2 * c2][e]);
-            pb[4 + e] = static_cast<bf16>(s[2 * c2 + 1][e]);
-          }
-          const bf16* v0 = &Vs[(32 * c2 + 4 * grp + (col >> 2)) * VS + 4 * (col & 3)];
-#pragma unroll
-          for (int n = 0; n < NDV; ++n) {
-            const bf16x8 va = cat8(lds_read_tr4(v0 + 16 * n), lds_read_tr4(v0 + 16 * VS + 16 * n));
-            acc[nb][n] = mfma32(va, pb, c2 == 0 ? acc[nb][n] * alpha : acc[nb][n]);
-          }
-        }
-      }
+      compute(blk, (blk >> 5) - wb, cur);
+    };
+    if (nbl > 0) issue(blist[0], kv0);
+    if (nbl > 1) issue(blist[1], kv1);
+    for (int bi = 0; bi < nbl; bi += 3) {
+      step(bi, kv0, kv2);
+      if (bi + 1 < nbl) step(bi + 1, kv1, kv0);
+      if (bi + 2 < nbl) step(bi + 2, kv2, kv1);
     }
   }
 
