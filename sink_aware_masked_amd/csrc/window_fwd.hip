@@ -115,13 +115,15 @@ void window_fwd_bf16(const Params p) {
   constexpr int NLD = (C::KT * CH + 255) / 256;
   const bf16* kh = kg + (int64_t)kvh * p.k_head;
   const bf16* vh = vg + (int64_t)kvh * p.v_head;
-  int koff[NLD], voff[NLD];
+  int koff[NLD], voff[NLD], lk[NLD], lv[NLD];  // global byte offsets, LDS element offsets
 #pragma unroll
   for (int u = 0; u < NLD; ++u) {
     const int t = tid + 256 * u;
     const int r = t / CH, c = t - r * CH;
     koff[u] = (int)((r * p.k_row + 8 * c) * 2);
     voff[u] = (int)((r * p.v_row + 8 * c) * 2);
+    lk[u] = r * C::KS + 8 * c;
+    lv[u] = r * C::VS + 8 * c;
   }
   bf16x8 kr[NLD], vr[NLD];
   auto load_tile = [&](int kt0) {
@@ -139,11 +141,9 @@ void window_fwd_bf16(const Params p) {
   auto store_tile = [&]() {
 #pragma unroll
     for (int u = 0; u < NLD; ++u) {
-      const int t = tid + 256 * u;
-      if (t < C::KT * CH) {
-        const int r = t / CH, c = t - r * CH;
-        *reinterpret_cast<bf16x8*>(&Ks[r * C::KS + 8 * c]) = kr[u];
-        *reinterpret_cast<bf16x8*>(&Vs[r * C::VS + 8 * c]) = vr[u];
+      if (tid + 256 * u < C::KT * CH) {
+        *reinterpret_cast<bf16x8*>(&Ks[lk[u]]) = kr[u];
+        *reinterpret_cast<bf16x8*>(&Vs[lv[u]]) = vr[u];
       }
     }
   };
