@@ -4,246 +4,381 @@
 // first key; DeepSeek-V4 sparse-MLA page: the null-logit fold after the key
 // loop).
 //
-// One workgroup = 64 consecutive packed query rows x one query head; 4 waves
-// of 16 rows.  The key band of the tile, [lo(first row), hi(last row)], is
-// staged through LDS in 64-key tiles (K and V row-major, coalesced 16-byte
-// loads).  Per wave and 16-key sub-block:
-//   S^T[key][row] = K[key][:] . Q[row][:]        (MFMA 16x16x32 bf16, Q in VGPRs)
-// so every lane owns one query row; masking is two integer compares against
-// the row's window [lo, hi]; the key-0 bias is one compare against the row's
-// sequence start.  P (bf16) then feeds
-//   O^T[dv][row] += V^T[dv][key] . P^T[key][row] (MFMA 16x16x32 bf16)
-// where V^T comes straight from the row-major V tile through the transposing
-// LDS read, so V is never transposed in memory.  Sub-blocks outside a wave's
-// band are skipped (wave-uniform).
+// One workgroup = 128 consecutive packed query rows x one query head; 4 waves
+// of 32 rows.  The key band of the workgroup, [lo(first row), hi(last row)],
+// streams through a ring of LDS slots, 64 keys (K tile then V tile) per slot,
+// filled by direct-to-LDS loads that are all issued ahead: with a 64-key
+// window the whole band (256 keys) is in flight before the first MFMA.  The
+// Q tile itself arrives the same way, in the ring's last slot, and moves to
+// VGPRs before that slot is reused.  Per wave and 32-key block:
+//   S^T[key][row] = K[key][:] . Q[row][:]          (MFMA 32x32x16 bf16)
+// so every lane owns one query row and 16 of the block's keys; masking is two
+// integer compares against the row's window; the key-0 bias is one compare
+// against the row's sequence start.  P (bf16) then feeds
+//   O^T[dv][row] += V^T[dv][key] . P^T[key][row]   (MFMA 32x32x16 bf16)
+// with V^T read straight from the row-major V tile by the transposing LDS
+// read.  Blocks outside a wave's band are skipped (wave-uniform).
+//
+// LDS layout: rows of D bf16 (D/8 16-byte chunks), chunk c of row r stored at
+// chunk (c + rot(r)) mod (D/8).  The K rotation makes the 16 rows read by one
+// 16-lane quarter of a 16-byte MFMA operand read land in 16 different bank
+// groups; the V rotation does the same for the 4 rows x 64 bytes that half a
+// wave reads with one transposing read.  For D = 80 the V rows of one
+// transposing read are taken two apart (keys 0,2,4,6 | 1,3,5,7 of each group
+// of 8): that order is conflict-free with no rotation at all.  The key order
+// inside a 32-key block is free (softmax and P.V sum over keys), so it is
+// applied alike to the K rows of S^T and the V rows of P.V.
 #include "common.hpp"
 
 namespace attn {
 
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float floatx16;
+
+__device__ __forceinline__ floatx16 mfma32x32(bf16x8 a, bf16x8 b, floatx16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
 template <int D>
 struct WinCfg {
-  static constexpr int BM = 64;                     // query rows per workgroup
-  static constexpr int KT = 64;                     // keys per LDS tile
-  static constexpr int NC32 = D / 32;               // full 32-wide head-dim chunks
-  static constexpr bool TAIL16 = (D % 32) == 16;    // one 16-wide tail chunk
-  static constexpr int NDV = D / 16;                // 16-wide output column blocks
-  // Row strides (elements) chosen so that the 16-byte K reads of 8 consecutive
-  // rows and the 4-row transposing V reads each hit distinct LDS banks.
-  static constexpr int KS = D + 8;
-  static constexpr int VS = (((D / 2) % 32) == 8 || ((D / 2) % 32) == 24) ? D : D + 16;
-  // Waves per SIMD the register budget is held to: 4 resident workgroups per
-  // CU keep 4 x 64 rows of one tile in flight for the small head dims.
-  static constexpr int WAVES = D <= 96 ? 4 : 3;
+  static constexpr int BM = 128;                 // query rows per workgroup (4 waves x 32)
+  static constexpr int KT = 64;                  // keys per ring slot
+  static constexpr int NCH = D / 8;              // 16-byte chunks per row
+  static constexpr int NQK = D / 16;             // 32x32x16 MFMAs per block for S^T
+  static constexpr int NB = (D + 31) / 32;       // 32-wide column blocks of O^T
+  static constexpr int ROWB = NCH * 16;          // bytes per LDS row
+  static constexpr int SLOT = 2 * KT * ROWB;     // K tile + V tile; equals the 128-row Q tile
+  static constexpr int NS = D == 64 ? 5 : D == 80 ? 4 : D == 96 ? 3 : 2;  // slots: <= 80 KB, 2 workgroups per CU
+  static constexpr int NPW = SLOT / 1024 / 4;    // 1 KB direct-to-LDS loads per wave per slot
+  static constexpr bool ILV = (D == 80);         // keys two apart in one transposing read
+  static_assert(NPW * 4 * 1024 == SLOT, "slot is a whole number of wave loads");
+  static_assert(NS * SLOT <= 80 * 1024, "two workgroups per CU");
+  static_assert(BM * (D + 8) * 2 <= NS * SLOT, "output staging fits the ring");
 };
 
+// Chunk rotation of row r for K / Q tiles.  Row r starts at chunk phase
+// (D/8) r mod 16 of the 256-byte bank space; the rows that share a phase
+// (period P = 16 / gcd(D/8, 16)) are shifted apart by one chunk each, so 16
+// consecutive rows read at the same logical chunk hit 16 distinct phases.
+template <int D>
+__device__ __forceinline__ int rot_k(int r) {
+  constexpr int nch = D / 8;
+  constexpr int g = (nch % 16 == 0) ? 16 : (nch % 8 == 0) ? 8 : (nch % 4 == 0) ? 4 : 2;
+  constexpr int P = 16 / g;
+  return (r / P) & (16 / P - 1);
+}
+template <int D>
+__device__ __forceinline__ int rot_v(int r) {
+  if (D == 64) return ((r >> 1) & 1) * 4;
+  if (D == 128) return (r & 3) * 4;
+  return 0;
+}
+// position (0..7) inside an aligned group of 8 keys for MFMA row m % 8
+template <int D>
+__device__ __forceinline__ int key_in8(int m) {
+  return WinCfg<D>::ILV ? (((m & 3) << 1) | ((m >> 2) & 1)) : m;
+}
+
+template <int N>
+__device__ __forceinline__ void wait_tiles(int k) {  // k later tiles may stay in flight
+  if (k >= 3) wait_vmcnt<3 * N>();
+  else if (k == 2) wait_vmcnt<2 * N>();
+  else if (k == 1) wait_vmcnt<N>();
+  else wait_vmcnt<0>();
+}
+
+__device__ __forceinline__ float swap_halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float swap_halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 template <int D, int SINK>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WinCfg<D>::WAVES, WinCfg<D>::WAVES)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void window_fwd_bf16(const Params p) {
   using C = WinCfg<D>;
-  static_assert(D % 16 == 0 && D <= 256, "head dim");
-  __shared__ __attribute__((aligned(16))) bf16 Ks[C::KT * C::KS];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[C::KT * C::VS];
+  static_assert(D % 16 == 0 && D <= 128, "head dim");
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[C::NS * C::SLOT];
 
   const int b = xcd_remap(blockIdx.x, gridDim.x);
-  const int tile = b % p.num_tiles;
-  const int h = b / p.num_tiles;
+  // tile-major: the heads of one row tile are neighbours, so an XCD's L2
+  // holds whole K/V rows (all heads) of a few consecutive tiles
+  const int tile = b / p.Hq;
+  const int h = b - tile * p.Hq;
   const int kvh = h / p.group;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
-  const int col = lane & 15, grp = lane >> 4;
+  const int n = lane & 31, hf = lane >> 5;                      // MFMA column (row of the wave), half
   const int r0 = tile * C::BM;
   const int rlast = min(r0 + C::BM - 1, p.T - 1);
-  const int i = r0 + wave * 16 + col;  // this lane's query row
+  const int r0w = r0 + 32 * wave;
+  const bool wave_active = r0w <= rlast;
 
-  // Window of every row: [max(seq start, i - W), min(seq end - 1, i + W)].
-  auto row_window = [&](int row, int& lo, int& hi, int& start) {
-    const int s = find_segment(p.cu, p.num_seqs, row);
-    start = __ldg(p.cu + s);
-    lo = max(start, row - p.window);
-    hi = min(__ldg(p.cu + s + 1) - 1, row + p.window);
-  };
-  int lo = 1, hi = 0, key0 = -1;
-  if (i < p.T) row_window(i, lo, hi, key0);
-  // lo and hi are non-decreasing in the row index, so the band of a set of
-  // consecutive rows is [lo(first), hi(last)].
-  int kmin, kmax, tmp;
-  row_window(r0, kmin, tmp, tmp);
-  row_window(rlast, tmp, kmax, tmp);
-  // This wave's band [wlo, whi]; its interior [lo of the last row, hi of the
-  // first row] is valid for every row of the wave, so sub-blocks inside it
-  // need no per-element mask; key-0 positions of the wave lie in [k0a, k0b].
-  int wlo = 0x7fffffff, whi = -1, ilo = 0x7fffffff, ihi = -1, k0a = -1, k0b = -1;
-  {
-    const int wr0 = r0 + wave * 16;
-    if (wr0 <= rlast) {
-      row_window(wr0, wlo, ihi, k0a);
-      row_window(min(wr0 + 15, rlast), ilo, whi, k0b);
-    }
+  // ---- windows.  Sequences touching this tile: sa .. sb (scalar loads only,
+  // so no vector load is pending once the ring is in flight).
+  const int sa = find_segment(p.cu, p.num_seqs, r0);
+  const int sb = find_segment(p.cu, p.num_seqs, rlast);
+  const int kmin = max(__ldg(p.cu + sa), r0 - p.window);
+  const int kmax = min(__ldg(p.cu + sb + 1) - 1, rlast + p.window);
+  const int ri = min(r0w + n, rlast);  // this lane's row (clamped past the end)
+  int start = 0, end = 1;
+  for (int s = sa; s <= sb; ++s) {
+    const int cs = __ldg(p.cu + s), ce = __ldg(p.cu + s + 1);
+    if (ri >= cs && ri < ce) { start = cs; end = ce; }
   }
+  const int lo = max(start, ri - p.window);
+  const int hi = min(end - 1, ri + p.window);
+  // Rows, lo and hi are non-decreasing along the lanes 0..31.  Wave band
+  // [wlo, whi]; interior [ilo, ihi] valid for every row of the wave; key-0
+  // positions (sequence starts) of the wave lie in [k0a, k0b].
+  const int wlo = __builtin_amdgcn_readlane(lo, 0), whi = __builtin_amdgcn_readlane(hi, 31);
+  const int ilo = __builtin_amdgcn_readlane(lo, 31), ihi = __builtin_amdgcn_readlane(hi, 0);
+  const int k0a = __builtin_amdgcn_readlane(start, 0), k0b = __builtin_amdgcn_readlane(start, 31);
+  const int ntiles = (kmax - kmin + C::KT) / C::KT;
 
-  // Q^T fragments (B operand): lane holds row i, dims 32c + 8*grp + [0, 8).
-  const bf16* qg = static_cast<const bf16*>(p.q);
-  const bf16* kg = static_cast<const bf16*>(p.k);
-  const bf16* vg = static_cast<const bf16*>(p.v);
-  bf16x8 qf[C::NC32 > 0 ? C::NC32 : 1];
-  bf16x4 qt = {};
-  {
-    const bf16* qrow = qg + (int64_t)min(i, p.T - 1) * p.q_row + (int64_t)h * p.q_head;
-#pragma unroll
-    for (int c = 0; c < C::NC32; ++c) {
-      qf[c] = *reinterpret_cast<const bf16x8*>(qrow + 32 * c + 8 * grp);
-      if (i >= p.T) qf[c] = bf16x8{};
-    }
-    if (C::TAIL16) {
-      qt = *reinterpret_cast<const bf16x4*>(qrow + 32 * C::NC32 + 4 * grp);
-      if (i >= p.T) qt = bf16x4{};
-    }
-  }
-
-  const float sl2 = p.scale_log2;
+  // The kernel works with sl2 > 0: a negative scale is moved into Q's sign
+  // (exact), and a zero scale becomes the least normal float, which leaves
+  // every finite logit within 2^-100 of zero, so its exp2 rounds to 1 just as
+  // for the exact zero logits.
+  const bool neg_scale = p.scale_log2 < 0.0f;
+  const float sl2 = fmaxf(fabsf(p.scale_log2), __FLT_MIN__);
   const float bias2 = (SINK == kSinkKey0) ? __ldg(p.sinks + h) * kLog2e : 0.0f;
+  const float sink2 = (SINK == kSinkNull) ? __ldg(p.sinks + h) * kLog2e : 0.0f;
+
+  // ---- ring filling.  Direct-to-LDS load i of a slot (i = wave*NPW + u)
+  // writes slot bytes [1024 i, 1024 i + 1024); lane l's 16 bytes land at
+  // 1024 i + 16 l, i.e. physical chunk q = 64 i + l of the slot.
+  const char* kg = static_cast<const char*>(p.k) + (int64_t)kvh * p.k_head * 2;
+  const char* vg = static_cast<const char*>(p.v) + (int64_t)kvh * p.v_head * 2;
+  const char* qg = static_cast<const char*>(p.q) + (int64_t)h * p.q_head * 2;
+  const int64_t krow = p.k_row * 2, vrow = p.v_row * 2, qrow = p.q_row * 2;
+  const uint32_t sbase = lds_addr(smem);
+  int trow[C::NPW], tc16[C::NPW];  // per load: row inside the tile, source chunk byte offset
+#pragma unroll
+  for (int u = 0; u < C::NPW; ++u) {
+    const int i = wave * C::NPW + u;
+    const bool isv = i >= C::NCH;
+    const int q = 64 * (isv ? i - C::NCH : i) + lane;
+    const int r = q / C::NCH, s = q - r * C::NCH;
+    const int rot = isv ? rot_v<D>(r) : rot_k<D>(r);
+    trow[u] = r;
+    tc16[u] = 16 * ((s - rot + C::NCH) % C::NCH);
+  }
+  auto issue = [&](int t, int slot) {
+    const int kt0 = kmin + C::KT * t;
+#pragma unroll
+    for (int u = 0; u < C::NPW; ++u) {
+      const int i = wave * C::NPW + u;
+      const bool isv = i >= C::NCH;
+      const int row = min(kt0 + trow[u], kmax);  // rows past the band repeat its last key
+      const char* g = (isv ? vg + row * vrow : kg + row * krow) + tc16[u];
+      load_lds16_m0(g, sbase + slot * C::SLOT + 1024 * i);
+    }
+  };
+  // Q tile (128 rows) into the last slot, K rotation.
+#pragma unroll
+  for (int u = 0; u < C::NPW; ++u) {
+    const int i = wave * C::NPW + u;
+    const int q = 64 * i + lane;
+    const int r = q / C::NCH, s = q - r * C::NCH;
+    const int row = min(r0 + r, p.T - 1);
+    load_lds16_m0(qg + row * qrow + 16 * ((s - rot_k<D>(r) + C::NCH) % C::NCH),
+                  sbase + (C::NS - 1) * C::SLOT + 1024 * i);
+  }
+#pragma unroll
+  for (int t = 0; t < C::NS - 1; ++t)
+    if (t < ntiles) issue(t, t);
+
+  // ---- per-lane LDS read offsets (bytes, relative to a slot / the Q region)
+  constexpr int KSTEP = C::ILV ? 2 : 1;
+  const int kr = (n & ~7) | key_in8<D>(n & 7);  // K row of MFMA row n in a 32-key block
+  int kofs[C::NQK], qofs[C::NQK], vofs[C::NB];
+#pragma unroll
+  for (int d = 0; d < C::NQK; ++d) {
+    const int c = 2 * d + hf;
+    kofs[d] = kr * C::ROWB + 16 * ((c + rot_k<D>(kr)) % C::NCH);
+    const int qr = 32 * wave + n;
+    qofs[d] = qr * C::ROWB + 16 * ((c + rot_k<D>(qr)) % C::NCH);
+  }
+  {
+    const int j = lane & 15;
+    const int vr = key_in8<D>(4 * hf + (j >> 2));  // V row (inside 8) of transposing-read row j/4
+#pragma unroll
+    for (int nb = 0; nb < C::NB; ++nb) {
+      int col = 32 * nb + 16 * ((lane >> 4) & 1) + 4 * (j & 3);
+      if (col >= D) col -= 16;  // D % 32 == 16: the upper half block duplicates (never stored)
+      vofs[nb] = vr * C::ROWB + 16 * ((col / 8 + rot_v<D>(vr)) % C::NCH) + 2 * (col % 8);
+    }
+  }
+  // key offset (inside a 32-key block) of accumulator element e: kbase_l + kc(e)
+  const int kbase_l = C::ILV ? hf : 4 * hf;
+
+  bf16x8 qf[C::NQK];
   float m2 = kNegInf, lsum = 0.0f;
-  floatx4 acc[C::NDV];
+  floatx16 acc[C::NB];
 #pragma unroll
-  for (int n = 0; n < C::NDV; ++n) acc[n] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[nb][e] = 0.0f;
 
-  // K/V staging: every thread owns NLD 16-byte chunks of each tile, fetched
-  // with range-checked buffer loads (rows past the band come back as zeros).
-  // The next tile's loads are issued right after the current tile is written
-  // to LDS, so their latency overlaps this tile's MFMA work.
-  constexpr int CH = D / 8;                          // 16-byte chunks per row
-  constexpr int NLD = (C::KT * CH + 255) / 256;
-  const bf16* kh = kg + (int64_t)kvh * p.k_head;
-  const bf16* vh = vg + (int64_t)kvh * p.v_head;
-  int koff[NLD], voff[NLD], lk[NLD], lv[NLD];  // global byte offsets, LDS element offsets
+  const bf16* lds = reinterpret_cast<const bf16*>(smem);
+  auto compute = [&](int t, int slot) {
+    const int kt0 = kmin + C::KT * t;
+    if (!wave_active || kt0 > whi || kt0 + C::KT - 1 < wlo) return;  // wave-uniform
+    const int kb = slot * C::SLOT, vb = kb + C::KT * C::ROWB;
+    // Per 32-key block (all flags wave-uniform): live = overlaps the wave's
+    // band; inside = inside every row's window (no mask); k0 = holds a key-0
+    // column of some row.  x keeps the raw dot products (masked ones -inf);
+    // the scale, the key-0 bias and the reference max all go into one fma in
+    // the exponent, so a zero bias gives bit for bit the no-sink numbers.
+    float x[2][16], bm[2];
+    bool live[2], k0[2];
 #pragma unroll
-  for (int u = 0; u < NLD; ++u) {
-    const int t = tid + 256 * u;
-    const int r = t / CH, c = t - r * CH;
-    koff[u] = (int)((r * p.k_row + 8 * c) * 2);
-    voff[u] = (int)((r * p.v_row + 8 * c) * 2);
-    lk[u] = r * C::KS + 8 * c;
-    lv[u] = r * C::VS + 8 * c;
-  }
-  bf16x8 kr[NLD], vr[NLD];
-  auto load_tile = [&](int kt0) {
-    const int rows = min(C::KT, kmax - kt0 + 1);
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kh + (int64_t)kt0 * p.k_row, (int)(rows * p.k_row * 2));
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vh + (int64_t)kt0 * p.v_row, (int)(rows * p.v_row * 2));
+    for (int blk = 0; blk < 2; ++blk) {
+      const int kb0 = kt0 + 32 * blk;
+      live[blk] = kb0 <= whi && kb0 + 31 >= wlo;
+      k0[blk] = SINK == kSinkKey0 && kb0 <= k0b && kb0 + 31 >= k0a;
+      bm[blk] = kNegInf;
+      if (!live[blk]) continue;
+      floatx16 s = {};
 #pragma unroll
-    for (int u = 0; u < NLD; ++u) {
-      if (tid + 256 * u < C::KT * CH) {
-        kr[u] = buf_load16(rk, koff[u]);
-        vr[u] = buf_load16(rv, voff[u]);
+      for (int d = 0; d < C::NQK; ++d)
+        s = mfma32x32(*reinterpret_cast<const bf16x8*>(lds + (kb + 32 * blk * C::ROWB + kofs[d]) / 2), qf[d], s);
+      if (kb0 >= ilo && kb0 + 31 <= ihi) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) x[blk][e] = s[e];
+      } else {
+        const int vlo = lo - kb0 - kbase_l, vhi = hi - kb0 - kbase_l;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int kc = 8 * (e >> 2) + KSTEP * (e & 3);
+          x[blk][e] = ((kc >= vlo) & (kc <= vhi)) ? s[e] : kNegInf;
+        }
       }
-    }
-  };
-  auto store_tile = [&]() {
+      float m = kNegInf;
+      if (k0[blk]) {
+        const int dk = start - kb0 - kbase_l;
 #pragma unroll
-    for (int u = 0; u < NLD; ++u) {
-      if (tid + 256 * u < C::KT * CH) {
-        *reinterpret_cast<bf16x8*>(&Ks[lk[u]]) = kr[u];
-        *reinterpret_cast<bf16x8*>(&Vs[lv[u]]) = vr[u];
+        for (int e = 0; e < 16; ++e) {
+          const int kc = 8 * (e >> 2) + KSTEP * (e & 3);
+          m = fmaxf(m, __builtin_fmaf(x[blk][e], sl2, kc == dk ? bias2 : 0.0f));
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) m = fmaxf(m, x[blk][e]);
+        m *= sl2;  // sl2 > 0: the max commutes with the scaling
       }
-    }
-  };
-
-  load_tile(kmin);
-  for (int kt0 = kmin; kt0 <= kmax; kt0 += C::KT) {
-    __syncthreads();  // the previous tile has been consumed
-    store_tile();
-    __syncthreads();
-    if (kt0 + C::KT <= kmax) load_tile(kt0 + C::KT);
-    if (kt0 > whi || kt0 + C::KT - 1 < wlo) continue;  // wave-uniform
-
-    float s[4][4];
-    bool live[4];
-#pragma unroll
-    for (int sb = 0; sb < 4; ++sb) {
-      const int kb0 = kt0 + 16 * sb;
-      live[sb] = !(kb0 > whi || kb0 + 15 < wlo);
-      if (!live[sb]) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) s[sb][e] = kNegInf;
-        continue;
-      }
-      floatx4 a = {0.f, 0.f, 0.f, 0.f};
-      const bf16* krow = &Ks[(16 * sb + col) * C::KS];
-#pragma unroll
-      for (int c = 0; c < C::NC32; ++c)
-        a = mfma32(*reinterpret_cast<const bf16x8*>(krow + 32 * c + 8 * grp), qf[c], a);
-      if (C::TAIL16)
-        a = mfma16(*reinterpret_cast<const bf16x4*>(krow + 32 * C::NC32 + 4 * grp), qt, a);
-      const bool interior = kb0 >= ilo && kb0 + 15 <= ihi;          // wave-uniform
-      const bool has_key0 = SINK == kSinkKey0 && kb0 <= k0b && kb0 + 15 >= k0a;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int j = kb0 + 4 * grp + e;
-        float x = a[e] * sl2;
-        // bitwise (not short-circuit) logic: one select per element, no
-        // divergent branches between the MFMA and the read of its result
-        if (SINK == kSinkKey0) x += (has_key0 & (j == key0)) ? bias2 : 0.0f;
-        s[sb][e] = (interior | ((j >= lo) & (j <= hi))) ? x : kNegInf;
-      }
+      bm[blk] = m;
     }
 
-    // online softmax (exp2 domain); every lane owns one row, 16 of its keys
-    float mt = kNegInf;
-#pragma unroll
-    for (int sb = 0; sb < 4; ++sb)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) mt = fmaxf(mt, s[sb][e]);
-    mt = max_over_groups(mt);
+    // online softmax, exp2 domain, lazy reference max
+    const float mt = swap_halves_max(fmaxf(bm[0], bm[1]));
     const float mn = fmaxf(m2, mt);
-    const float mu = (mn == kNegInf) ? 0.0f : mn;
-    const float alpha = exp2f_fast(m2 - mu);
-    float ps = 0.0f;
+    const bool move = mn > m2 + kRescaleLog2;  // also m2 == -inf < mn
+    if (__ballot(move) != 0) {
+      const float alpha = move ? exp2f_fast(m2 - mn) : 1.0f;
+      if (move) m2 = mn;
+      lsum *= alpha;
 #pragma unroll
-    for (int sb = 0; sb < 4; ++sb)
+      for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        s[sb][e] = exp2f_fast(s[sb][e] - mu);
-        ps += s[sb][e];
-      }
-    lsum = lsum * alpha + ps;
-    m2 = mn;
-    if (__ballot(alpha != 1.0f) != 0) {  // skip the rescale when no row's max moved
-#pragma unroll
-      for (int n = 0; n < C::NDV; ++n) acc[n] *= alpha;
+        for (int e = 0; e < 16; ++e) acc[nb][e] *= alpha;
     }
+    const float mu = (m2 == kNegInf) ? 0.0f : m2;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      if (!live[blk]) continue;
+      if (k0[blk]) {
+        const int dk = start - (kt0 + 32 * blk) - kbase_l;
+        const float bmu = bias2 - mu;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int kc = 8 * (e >> 2) + KSTEP * (e & 3);
+          x[blk][e] = exp2f_fast(__builtin_fmaf(x[blk][e], sl2, kc == dk ? bmu : -mu));
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) x[blk][e] = exp2f_fast(__builtin_fmaf(x[blk][e], sl2, -mu));
+      }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) lsum += x[blk][e];
 
 #pragma unroll
-    for (int c2 = 0; c2 < 2; ++c2) {
-      if (!live[2 * c2] && !live[2 * c2 + 1]) continue;
-      bf16x8 pb;
+      for (int c2 = 0; c2 < 2; ++c2) {
+        bf16x8 pb;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        pb[e] = static_cast<bf16>(s[2 * c2][e]);
-        pb[4 + e] = static_cast<bf16>(s[2 * c2 + 1][e]);
-      }
-      const bf16* v0 = &Vs[(32 * c2 + 4 * grp + (col >> 2)) * C::VS + 4 * (col & 3)];
+        for (int e = 0; e < 8; ++e) pb[e] = static_cast<bf16>(x[blk][8 * c2 + e]);
+        const int rb = vb + (32 * blk + 16 * c2) * C::ROWB;
 #pragma unroll
-      for (int n = 0; n < C::NDV; ++n) {
-        const bf16x8 va = cat8(lds_read_tr4(v0 + 16 * n), lds_read_tr4(v0 + 16 * C::VS + 16 * n));
-        acc[n] = mfma32(va, pb, acc[n]);
+        for (int nb = 0; nb < C::NB; ++nb) {
+          const bf16* v0 = lds + (rb + vofs[nb]) / 2;
+          const bf16x8 va = cat8(lds_read_tr4(v0), lds_read_tr4(v0 + 8 * C::ROWB / 2));
+          acc[nb] = mfma32x32(va, pb, acc[nb]);
+        }
       }
     }
+  };
+
+  // ---- key loop over the ring.  Step t: tile t has landed (this wave's
+  // loads by vmcnt, every wave's by the barrier), which also means every wave
+  // is done with tile t-1, so its slot takes tile t + NS - 1.
+  for (int t = 0; t < ntiles; ++t) {
+    wait_tiles<C::NPW>(min(C::NS - 2, ntiles - 1 - t));
+    lds_barrier();
+    if (t == 0) {
+#pragma unroll
+      for (int d = 0; d < C::NQK; ++d)
+        qf[d] = *reinterpret_cast<const bf16x8*>(lds + ((C::NS - 1) * C::SLOT + qofs[d]) / 2);
+      if (neg_scale) {
+#pragma unroll
+        for (int d = 0; d < C::NQK; ++d) {
+          typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4;
+          qf[d] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, qf[d]) ^ 0x80008000u);
+        }
+      }
+      lds_barrier();  // the Q slot is free once every wave holds its fragments
+    }
+    if (t + C::NS - 1 < ntiles) issue(t + C::NS - 1, (t + C::NS - 1) % C::NS);
+    compute(t, t % C::NS);
   }
 
-  lsum = sum_over_groups(lsum);
-  if (i < p.T) {
-    const float sink2 = (SINK == kSinkNull) ? __ldg(p.sinks + h) * kLog2e : 0.0f;
-    const float f = sink_fold<SINK>(m2, lsum, sink2);
-    bf16* orow = static_cast<bf16*>(p.out) + (int64_t)i * p.o_row + (int64_t)h * p.o_head;
+  // ---- epilogue.  O^T leaves the accumulators as 4-element pieces of 32
+  // different rows; written out directly those would be 16-byte fragments of
+  // partial cache lines.  Each wave stages its 32 x D tile in LDS (rows
+  // padded by 8 elements against bank conflicts) and stores it back row-major,
+  // 16 bytes per lane, every row one contiguous run.
+  lsum = swap_halves_sum(lsum);
+  const float f = sink_fold<SINK>(m2, lsum, sink2);
+  lds_barrier();  // every wave is done with the ring
+  constexpr int OS = D + 8;
+  bf16* ost = reinterpret_cast<bf16*>(smem) + wave * 32 * OS;
 #pragma unroll
-    for (int n = 0; n < C::NDV; ++n) {
-      bf16x4 o;
+  for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] = static_cast<bf16>(acc[n][e] * f);
-      *reinterpret_cast<bf16x4*>(orow + 16 * n + 4 * grp) = o;
+    for (int q = 0; q < 4; ++q) {
+      const int dv = 32 * nb + 8 * q + 4 * hf;
+      if (dv < D) {
+        bf16x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = static_cast<bf16>(acc[nb][4 * q + e] * f);
+        *reinterpret_cast<bf16x4*>(ost + n * OS + dv) = o;
+      }
     }
-    if (grp == 0) p.lse[(int64_t)h * p.T + i] = lse_natural(m2, lsum);
+  bf16* og = static_cast<bf16*>(p.out) + (int64_t)h * p.o_head;
+  constexpr int NCHUNK = 32 * C::NCH;  // 16-byte pieces of the wave's tile
+  static_assert(NCHUNK % 64 == 0, "whole wave stores");
+#pragma unroll
+  for (int u = 0; u < NCHUNK / 64; ++u) {
+    const int c = lane + 64 * u;
+    const int rr = c / C::NCH, cc = c - rr * C::NCH;
+    const int row = r0w + rr;
+    const bf16x8 v = *reinterpret_cast<const bf16x8*>(ost + rr * OS + 8 * cc);
+    if (row <= rlast) *reinterpret_cast<bf16x8*>(og + (int64_t)row * p.o_row + 8 * cc) = v;
   }
+  const int i = r0w + n;
+  if (hf == 0 && i <= rlast) p.lse[(int64_t)h * p.T + i] = lse_natural(m2, lsum);
 }
 
 template <int D>
