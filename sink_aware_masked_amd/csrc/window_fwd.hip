@@ -6,11 +6,10 @@
 //
 // One workgroup = 128 consecutive packed query rows x one query head; 4 waves
 // of 32 rows.  The key band of the workgroup, [lo(first row), hi(last row)],
-// streams through a ring of LDS slots, 64 keys (K tile then V tile) per slot,
-// filled by direct-to-LDS loads that are all issued ahead: with a 64-key
-// window the whole band (256 keys) is in flight before the first MFMA.  The
-// Q tile itself arrives the same way, in the ring's last slot, and moves to
-// VGPRs before that slot is reused.  Per wave and 32-key block:
+// streams through LDS slots, 64 keys (K tile then V tile) per slot, filled by
+// direct-to-LDS loads a round of slots at a time: with a 64-key window the
+// whole band (256 keys) is one round, in flight at once.  Q goes straight to
+// VGPRs.  Per wave and 32-key block:
 //   S^T[key][row] = K[key][:] . Q[row][:]          (MFMA 32x32x16 bf16)
 // so every lane owns one query row and 16 of the block's keys; masking is two
 // integer compares against the row's window; the key-0 bias is one compare
@@ -46,7 +45,7 @@ struct WinCfg {
   static constexpr int NQK = D / 16;             // 32x32x16 MFMAs per block for S^T
   static constexpr int NB = (D + 31) / 32;       // 32-wide column blocks of O^T
   static constexpr int ROWB = NCH * 16;          // bytes per LDS row
-  static constexpr int SLOT = 2 * KT * ROWB;     // K tile + V tile; equals the 128-row Q tile
+  static constexpr int SLOT = 2 * KT * ROWB;     // K tile + V tile
   static constexpr int NS = D == 64 ? 5 : D == 80 ? 4 : D == 96 ? 3 : 2;  // slots: <= 80 KB, 2 workgroups per CU
   static constexpr int NPW = SLOT / 1024 / 4;    // 1 KB direct-to-LDS loads per wave per slot
   static constexpr bool ILV = (D == 80);         // keys two apart in one transposing read
@@ -177,31 +176,20 @@ void window_fwd_bf16(const Params p) {
       load_lds16_m0(g, sbase + slot * C::SLOT + 1024 * i);
     }
   };
-  // Q tile (128 rows) into the last slot, K rotation.
+  // Q^T fragments (B operand) straight to VGPRs: lane (n, hf) holds row
+  // r0w + n, dims 16 d + 8 hf + [0, 8).
+  bf16x8 qf[C::NQK];
+  {
+    const char* qr = qg + (int64_t)min(r0w + n, rlast) * qrow;
 #pragma unroll
-  for (int u = 0; u < C::NPW; ++u) {
-    const int i = wave * C::NPW + u;
-    const int q = 64 * i + lane;
-    const int r = q / C::NCH, s = q - r * C::NCH;
-    const int row = min(r0 + r, p.T - 1);
-    load_lds16_m0(qg + row * qrow + 16 * ((s - rot_k<D>(r) + C::NCH) % C::NCH),
-                  sbase + (C::NS - 1) * C::SLOT + 1024 * i);
+    for (int d = 0; d < C::NQK; ++d) qf[d] = *reinterpret_cast<const bf16x8*>(qr + 32 * d + 16 * hf);
   }
-#pragma unroll
-  for (int t = 0; t < C::NS - 1; ++t)
-    if (t < ntiles) issue(t, t);
-
-  // ---- per-lane LDS read offsets (bytes, relative to a slot / the Q region)
+  // ---- per-lane LDS read offsets (bytes, relative to a slot)
   constexpr int KSTEP = C::ILV ? 2 : 1;
   const int kr = (n & ~7) | key_in8<D>(n & 7);  // K row of MFMA row n in a 32-key block
-  int kofs[C::NQK], qofs[C::NQK], vofs[C::NB];
+  int kofs[C::NQK], vofs[C::NB];
 #pragma unroll
-  for (int d = 0; d < C::NQK; ++d) {
-    const int c = 2 * d + hf;
-    kofs[d] = kr * C::ROWB + 16 * ((c + rot_k<D>(kr)) % C::NCH);
-    const int qr = 32 * wave + n;
-    qofs[d] = qr * C::ROWB + 16 * ((c + rot_k<D>(qr)) % C::NCH);
-  }
+  for (int d = 0; d < C::NQK; ++d) kofs[d] = kr * C::ROWB + 16 * ((2 * d + hf + rot_k<D>(kr)) % C::NCH);
   {
     const int j = lane & 15;
     const int vr = key_in8<D>(4 * hf + (j >> 2));  // V row (inside 8) of transposing-read row j/4
@@ -215,7 +203,6 @@ void window_fwd_bf16(const Params p) {
   // key offset (inside a 32-key block) of accumulator element e: kbase_l + kc(e)
   const int kbase_l = C::ILV ? hf : 4 * hf;
 
-  bf16x8 qf[C::NQK];
   float m2 = kNegInf, lsum = 0.0f;
   floatx16 acc[C::NB];
 #pragma unroll
@@ -321,27 +308,30 @@ void window_fwd_bf16(const Params p) {
     }
   };
 
-  // ---- key loop over the ring.  Step t: tile t has landed (this wave's
-  // loads by vmcnt, every wave's by the barrier), which also means every wave
-  // is done with tile t-1, so its slot takes tile t + NS - 1.
-  for (int t = 0; t < ntiles; ++t) {
-    wait_tiles<C::NPW>(min(C::NS - 2, ntiles - 1 - t));
+  // ---- key loop, in rounds of NS tiles.  A round's tiles are all issued at
+  // once; after one wait and one barrier every wave runs through its blocks
+  // of the round without further synchronisation, so no wave waits at a
+  // barrier for another wave's share of a tile it does not need itself.
+  // (A 64-key window on 128 rows is one round.)
+  bool first = true;
+  for (int t0 = 0; t0 < ntiles; t0 += C::NS) {
+    if (!first) lds_barrier();  // the previous round's slots are free
+#pragma unroll
+    for (int u = 0; u < C::NS; ++u)
+      if (t0 + u < ntiles) issue(t0 + u, u);
+    wait_vmcnt<0>();
     lds_barrier();
-    if (t == 0) {
+    if (first && neg_scale) {
 #pragma unroll
-      for (int d = 0; d < C::NQK; ++d)
-        qf[d] = *reinterpret_cast<const bf16x8*>(lds + ((C::NS - 1) * C::SLOT + qofs[d]) / 2);
-      if (neg_scale) {
-#pragma unroll
-        for (int d = 0; d < C::NQK; ++d) {
-          typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4;
-          qf[d] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, qf[d]) ^ 0x80008000u);
-        }
+      for (int d = 0; d < C::NQK; ++d) {
+        typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4;
+        qf[d] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, qf[d]) ^ 0x80008000u);
       }
-      lds_barrier();  // the Q slot is free once every wave holds its fragments
     }
-    if (t + C::NS - 1 < ntiles) issue(t + C::NS - 1, (t + C::NS - 1) % C::NS);
-    compute(t, t % C::NS);
+    first = false;
+#pragma unroll
+    for (int u = 0; u < C::NS; ++u)
+      if (t0 + u < ntiles) compute(t0 + u, u);
   }
 
   // ---- epilogue.  O^T leaves the accumulators as 4-element pieces of 32
