@@ -12,8 +12,8 @@
 // is staged once in LDS and used by every head.  The row's list is first
 // compacted in LDS (a workgroup prefix sum over the valid entries), so padding
 // costs one pass over the list and no key tiles.  Key tiles of 32 gathered
-// rows go straight from memory into a 3-stage LDS ring (direct-to-LDS loads,
-// two tiles in flight behind the one being computed, waited for explicitly),
+// rows go straight from memory into a 2-stage LDS ring (direct-to-LDS loads,
+// the next tile in flight behind the one being computed, waited for explicitly),
 // stored with a 16-byte chunk swizzle so both operand reads below are free of
 // bank conflicts.  Per tile and wave:
 //   S^T[key][head] = K[key][:576] . Q[head][:576]   (18 MFMA 16x16x32 per 16 keys;
@@ -34,21 +34,24 @@ constexpr int KT = 32;                           // keys per LDS tile
 constexpr int RCH = DQK / 8;                     // 72 16-byte chunks per latent row
 constexpr int TILE_CH = KT * RCH;                // 2304 chunks = 36 KB per tile
 constexpr int TILE_EL = TILE_CH * 8;             // bf16 elements per tile
-constexpr int NSTAGE = 3;                        // LDS ring depth
+constexpr int NSTAGE = 2;                        // LDS ring depth
 constexpr int LDPW = TILE_CH / 64 / NW;          // 9 direct-to-LDS loads per wave per tile
-constexpr int CHUNK = 2048;                      // list entries compacted per pass
+constexpr int CHUNK = 1024;                      // list entries compacted per pass
 constexpr int NQC = DQK / 32;                    // 18 Q^T fragments
 constexpr int NDV = DV / 16;                     // 32 output blocks
 constexpr int KPIPE = 4;                         // K operand reads kept in flight
 static_assert(TILE_CH % (64 * NW) == 0, "whole wave loads per tile");
 }  // namespace mla
 
+// Two workgroups per CU (LDS: 2 x 36 KB ring + a 4 KB index chunk; at most
+// 256 registers per lane), so while one waits on its gathers or sits in its
+// softmax the other keeps the matrix cores busy.
 template <int SINK>
-__global__ __launch_bounds__(256) void topk_mla_fwd_bf16(const Params p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void topk_mla_fwd_bf16(const Params p) {
   using namespace mla;
   __shared__ __attribute__((aligned(16))) bf16 ks0[TILE_EL];
   __shared__ __attribute__((aligned(16))) bf16 ks1[TILE_EL];
-  __shared__ __attribute__((aligned(16))) bf16 ks2[TILE_EL];
   __shared__ int kidx[CHUNK];
   __shared__ int wsum[NW];
 
@@ -128,9 +131,14 @@ __global__ __launch_bounds__(256) void topk_mla_fwd_bf16(const Params p) {
     const int ntiles = (nvalid + KT - 1) / KT;
     auto issue = [&](int t, bf16* st) {
       const uint32_t st_addr = lds_addr(st) + (uint32_t)(wave * LDPW * 1024);
+      // The per-load offsets are recomputed on every call: hoisted out of the
+      // key loop they would be spilled, and a spill reload is a vector memory
+      // load whose wait would also drain the gathers in flight.
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
 #pragma unroll
       for (int u = 0; u < LDPW; ++u) {
-        const int ch = (wave * LDPW + u) * 64 + lane;
+        const int ch = (wave * LDPW + u) * 64 + ln;
         const int r = ch / RCH, cc = ch - r * RCH;
         const int posr = t * KT + r;
         const int j = kidx[posr < nvalid ? posr : 0];
@@ -197,35 +205,49 @@ __global__ __launch_bounds__(256) void topk_mla_fwd_bf16(const Params p) {
       }
     };
 
-    // tile t lives in stage t % 3; the loop is unrolled by the ring depth so
+    // tile t lives in stage t % 2; the loop is unrolled by the ring depth so
     // every LDS access names its stage array at compile time
-    auto step = [&](int t, bf16* cur, bf16* ahead2) {
-      if (t + 1 < ntiles) wait_vmcnt<LDPW>(); else wait_vmcnt<0>();
+    auto step = [&](int t, bf16* cur, bf16* next) {
+      wait_vmcnt<0>();
       lds_barrier();  // tile t is in LDS for every wave; tile t-1's stage is free
-      if (t + 2 < ntiles) issue(t + 2, ahead2);
+      if (t + 1 < ntiles) issue(t + 1, next);
       compute(t, cur);
     };
     if (ntiles > 0) issue(0, ks0);
-    if (ntiles > 1) issue(1, ks1);
     for (int t = 0; t < ntiles; t += NSTAGE) {
-      step(t, ks0, ks2);
+      step(t, ks0, ks1);
       if (t + 1 < ntiles) step(t + 1, ks1, ks0);
-      if (t + 2 < ntiles) step(t + 2, ks2, ks1);
     }
   }
 
   lsum = sum_over_groups(lsum);
   const float sink2 = (SINK == kSinkNull) ? __ldg(p.sinks + h) * kLog2e : 0.0f;
   const float fct = sink_fold<SINK>(m2, lsum, sink2);
-  bf16* orow = static_cast<bf16*>(p.out) + (int64_t)i * p.o_row + (int64_t)h * p.o_head + 4 * grp;
+  if (grp == 0) p.lse[(int64_t)h * p.T + i] = lse_natural(m2, lsum);
+
+  // The 64 heads of a row are one contiguous 64 KB run of out.  Each wave
+  // stages its 16 x 512 tile in the (now idle) ring, rows padded by 8
+  // elements, and writes it back 16 bytes per lane in address order, so the
+  // stores are whole cache lines instead of 32-byte pieces of 16 rows.
+  constexpr int OS = DV + 8;
+  lds_barrier();  // every wave is done with the ring
+  bf16* ost = ks0 + wave * (HPW * OS);
+  static_assert(NW * HPW * OS <= 2 * TILE_EL, "staging fits the ring");
 #pragma unroll
   for (int n = 0; n < NDV; ++n) {
     bf16x4 o;
 #pragma unroll
     for (int e = 0; e < 4; ++e) o[e] = static_cast<bf16>(acc[n][e] * fct);
-    *reinterpret_cast<bf16x4*>(orow + 16 * n) = o;
+    *reinterpret_cast<bf16x4*>(ost + col * OS + 16 * n + 4 * grp) = o;
   }
-  if (grp == 0) p.lse[(int64_t)h * p.T + i] = lse_natural(m2, lsum);
+  bf16* og = static_cast<bf16*>(p.out) + (int64_t)i * p.o_row + (int64_t)(hg * HPB + wave * HPW) * p.o_head;
+#pragma unroll
+  for (int u = 0; u < HPW * DV / 8 / 64; ++u) {
+    const int c = lane + 64 * u;              // 16-byte piece of the wave's tile
+    const int hh = c / (DV / 8), cc = c - hh * (DV / 8);
+    *reinterpret_cast<bf16x8*>(og + (int64_t)hh * p.o_head + 8 * cc) =
+        *reinterpret_cast<const bf16x8*>(ost + hh * OS + 8 * cc);
+  }
 }
 
 hipError_t launch_topk_mla_bf16(const Params& p, int sink, hipStream_t st) {
