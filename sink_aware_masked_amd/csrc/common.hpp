@@ -148,14 +148,26 @@ __device__ __forceinline__ int swz16(int r) { return ((r & 3) << 1) | ((r >> 2) 
 // in range; the final normalisation uses the same reference.
 constexpr float kRescaleLog2 = 8.0f;
 
-// max / sum over the four 16-lane groups holding the same MFMA column
+// max / sum over the four 16-lane groups holding the same MFMA column.  The
+// lane exchanges are VALU permutes (v_permlane16_swap pairs group 0 with 1
+// and 2 with 3; v_permlane32_swap pairs lanes l and l + 32), not LDS round
+// trips.  Each step combines a value with its partner's, so every lane ends
+// with the same result (addition is commutative, so also bit for bit).
+__device__ __forceinline__ float combine_swap16(float x, bool sum) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float a = __uint_as_float(r[0]), b = __uint_as_float(r[1]);
+  return sum ? a + b : fmaxf(a, b);
+}
+__device__ __forceinline__ float combine_swap32(float x, bool sum) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float a = __uint_as_float(r[0]), b = __uint_as_float(r[1]);
+  return sum ? a + b : fmaxf(a, b);
+}
 __device__ __forceinline__ float max_over_groups(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16));
-  return fmaxf(x, __shfl_xor(x, 32));
+  return combine_swap32(combine_swap16(x, false), false);
 }
 __device__ __forceinline__ float sum_over_groups(float x) {
-  x += __shfl_xor(x, 16);
-  return x + __shfl_xor(x, 32);
+  return combine_swap32(combine_swap16(x, true), true);
 }
 
 // Segment s with cu[s] <= t < cu[s+1] (largest such s; empty segments are

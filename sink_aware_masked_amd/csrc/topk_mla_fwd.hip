@@ -40,6 +40,7 @@ constexpr int CHUNK = 1024;                      // list entries compacted per p
 constexpr int NQC = DQK / 32;                    // 18 Q^T fragments
 constexpr int NDV = DV / 16;                     // 32 output blocks
 constexpr int KPIPE = 4;                         // K operand reads kept in flight
+constexpr int VPIPE = 4;                         // V^T operand reads kept in flight
 static_assert(TILE_CH % (64 * NW) == 0, "whole wave loads per tile");
 }  // namespace mla
 
@@ -197,11 +198,18 @@ void topk_mla_fwd_bf16(const Params p) {
           pb[4 * sb + e] = static_cast<bf16>(pe);
         }
       lsum += ps;
+      // V^T operands run VPIPE blocks ahead of the MFMAs that use them
+      auto vload = [&](int n) {
+        const bf16* v0 = st + 64 * (n >> 2) + voff[n & 3];
+        return cat8(lds_read_tr4(v0), lds_read_tr4(v0 + 16 * DQK));
+      };
+      bf16x8 vb[VPIPE];
+#pragma unroll
+      for (int n = 0; n < VPIPE; ++n) vb[n] = vload(n);
 #pragma unroll
       for (int n = 0; n < NDV; ++n) {
-        const bf16* v0 = st + 64 * (n >> 2) + voff[n & 3];
-        const bf16x8 va = cat8(lds_read_tr4(v0), lds_read_tr4(v0 + 16 * DQK));
-        acc[n] = mfma32(va, pb, acc[n]);
+        acc[n] = mfma32(vb[n % VPIPE], pb, acc[n]);
+        if (n + VPIPE < NDV) vb[n % VPIPE] = vload(n + VPIPE);
       }
     };
 
