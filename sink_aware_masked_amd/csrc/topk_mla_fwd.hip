@@ -14,8 +14,8 @@
 // costs one pass over the list and no key tiles.  Key tiles of 32 gathered
 // rows go straight from memory into a 2-stage LDS ring (direct-to-LDS loads,
 // the next tile in flight behind the one being computed, waited for explicitly),
-// stored with a 16-byte chunk swizzle so both operand reads below are free of
-// bank conflicts.  Per tile and wave:
+// stored chunk-major so both operand reads below are free of bank conflicts.
+// Per tile and wave:
 //   S^T[key][head] = K[key][:576] . Q[head][:576]   (18 MFMA 16x16x32 per 16 keys;
 //                                                   Q of the wave's 16 heads in VGPRs)
 //   O^T[dv][head] += V^T[dv][key] . P^T[key][head]  (32 MFMAs; V^T read from the
@@ -74,17 +74,21 @@ void topk_mla_fwd_bf16(const Params p) {
     for (int c = 0; c < NQC; ++c) qf[c] = *reinterpret_cast<const bf16x8*>(qrow + 32 * c);
   }
 
-  // Per-lane LDS element offsets within a tile (see swz16): K operand rows
-  // 16*sb + col, 16-byte chunks 4*cc + grp; V^T rows 4*grp + col/4 (+16),
-  // chunk pairs 2n, 2n+1.
-  const int kfr = swz16(col);
-  const int k_even = col * DQK + 8 * (grp ^ kfr);
-  const int k_odd = col * DQK + 8 * ((4 + grp) ^ kfr);
-  const int vfr = ((col >> 2) << 1) | (grp & 1);
-  const int vrow = (4 * grp + (col >> 2)) * DQK + 4 * (col & 1);
-  int voff[4];
-#pragma unroll
-  for (int n4 = 0; n4 < 4; ++n4) voff[n4] = vrow + 8 * ((2 * n4 + ((col >> 1) & 1)) ^ vfr);
+  // Tile layout in LDS, chunk-major: 16-byte chunk c (dims 8c .. 8c+7) of
+  // tile row r sits at element 8 * (32 c + (r ^ 8 (c & 1))).  One 1-KB
+  // direct-to-LDS load then fills two chunk columns of all 32 rows, so a lane
+  // gathers the same row for every load of a tile (one index read, one row
+  // address per tile).  The K operand read of a 16-lane group is 16
+  // consecutive rows of one chunk (256 contiguous bytes); the transposing V
+  // reads of a half-wave cover 128 bytes in each of two chunk columns, which
+  // the row flip on odd columns puts in opposite halves of the bank space.
+  const int kofs = 8 * (32 * grp + (col ^ (8 * (grp & 1))));  // + 1024 per MFMA step, + 128 per 16 keys
+  int vofs;                                                   // + 512 per 16 dv, + 128 for keys + 16
+  {
+    const int par = (col >> 1) & 1, key = 4 * grp + (col >> 2);
+    vofs = 8 * (32 * par + (key ^ (8 * par))) + 4 * (col & 1);
+  }
+  const int drow = (lane & 31) ^ (8 * (lane >> 5));  // tile row this lane gathers
 
   const float sl2 = p.scale_log2;
   float m2 = kNegInf, lsum = 0.0f;
@@ -132,19 +136,12 @@ void topk_mla_fwd_bf16(const Params p) {
     const int ntiles = (nvalid + KT - 1) / KT;
     auto issue = [&](int t, bf16* st) {
       const uint32_t st_addr = lds_addr(st) + (uint32_t)(wave * LDPW * 1024);
-      // The per-load offsets are recomputed on every call: hoisted out of the
-      // key loop they would be spilled, and a spill reload is a vector memory
-      // load whose wait would also drain the gathers in flight.
-      int ln = lane;
-      asm volatile("" : "+v"(ln));
+      // load u of this wave fills chunk columns 2 (wave LDPW + u) and + 1
+      const int posr = t * KT + drow;
+      const int j = kidx[posr < nvalid ? posr : 0];
+      const bf16* g = kg + (int64_t)j * p.k_row + 8 * (lane >> 5) + 16 * LDPW * wave;
 #pragma unroll
-      for (int u = 0; u < LDPW; ++u) {
-        const int ch = (wave * LDPW + u) * 64 + ln;
-        const int r = ch / RCH, cc = ch - r * RCH;
-        const int posr = t * KT + r;
-        const int j = kidx[posr < nvalid ? posr : 0];
-        load_lds16_m0(kg + (int64_t)j * p.k_row + 8 * (cc ^ swz16(r)), st_addr + u * 1024);
-      }
+      for (int u = 0; u < LDPW; ++u) load_lds16_m0(g + 16 * u, st_addr + u * 1024);
     };
 
     // ---- one tile: S, online softmax with lazy rescale, PV
@@ -154,18 +151,15 @@ void topk_mla_fwd_bf16(const Params p) {
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb) {
         floatx4 a = {0.f, 0.f, 0.f, 0.f};
-        const bf16* krow = st + sb * 16 * DQK;
+        const bf16* krow = st + kofs + 128 * sb;
         bf16x8 kb[KPIPE];
 #pragma unroll
-        for (int cc = 0; cc < KPIPE; ++cc)
-          kb[cc] = *reinterpret_cast<const bf16x8*>(krow + 64 * (cc >> 1) + ((cc & 1) ? k_odd : k_even));
+        for (int cc = 0; cc < KPIPE; ++cc) kb[cc] = *reinterpret_cast<const bf16x8*>(krow + 1024 * cc);
 #pragma unroll
         for (int cc = 0; cc < NQC; ++cc) {
           a = mfma32(kb[cc % KPIPE], qf[cc], a);
           const int nx = cc + KPIPE;
-          if (nx < NQC)
-            kb[cc % KPIPE] =
-                *reinterpret_cast<const bf16x8*>(krow + 64 * (nx >> 1) + ((nx & 1) ? k_odd : k_even));
+          if (nx < NQC) kb[cc % KPIPE] = *reinterpret_cast<const bf16x8*>(krow + 1024 * nx);
         }
         const bool all_in = t0 + 16 * sb + 4 * grp + 3 < nvalid;
 #pragma unroll
@@ -200,8 +194,8 @@ void topk_mla_fwd_bf16(const Params p) {
       lsum += ps;
       // V^T operands run VPIPE blocks ahead of the MFMAs that use them
       auto vload = [&](int n) {
-        const bf16* v0 = st + 64 * (n >> 2) + voff[n & 3];
-        return cat8(lds_read_tr4(v0), lds_read_tr4(v0 + 16 * DQK));
+        const bf16* v0 = st + vofs + 512 * n;
+        return cat8(lds_read_tr4(v0), lds_read_tr4(v0 + 128));
       };
       bf16x8 vb[VPIPE];
 #pragma unroll
