@@ -64,12 +64,20 @@ void topk_mla_fwd_bf16(const Params p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   const int col = lane & 15, grp = lane >> 4;
   const int h = hg * HPB + wave * HPW + col;  // this lane's head
+  // 16-byte chunk (of 4 per 32 dims) that k-slot grp carries in the S^T
+  // MFMAs: groups 0, 1 take the even chunks and 2, 3 the odd ones, so the
+  // lanes that one pass of a 16-byte LDS read serves (lanes 0-7 with 24-31,
+  // 8-15 with 16-23, and the same in the upper half) see the same row flip
+  // (below) and land in opposite halves of the bank space
+  const int kperm = ((grp & 1) << 1) | (grp >> 1);
 
   const bf16* qg = static_cast<const bf16*>(p.q);
   const bf16* kg = static_cast<const bf16*>(p.k);
   bf16x8 qf[NQC];
   {
-    const bf16* qrow = qg + (int64_t)i * p.q_row + (int64_t)h * p.q_head + 8 * grp;
+    // k-slot grp of each MFMA step holds dims 32 c + 8 kperm + [0, 8); the
+    // same permutation on the K side (below) keeps the two operands in step
+    const bf16* qrow = qg + (int64_t)i * p.q_row + (int64_t)h * p.q_head + 8 * kperm;
 #pragma unroll
     for (int c = 0; c < NQC; ++c) qf[c] = *reinterpret_cast<const bf16x8*>(qrow + 32 * c);
   }
@@ -78,11 +86,11 @@ void topk_mla_fwd_bf16(const Params p) {
   // tile row r sits at element 8 * (32 c + (r ^ 8 (c & 1))).  One 1-KB
   // direct-to-LDS load then fills two chunk columns of all 32 rows, so a lane
   // gathers the same row for every load of a tile (one index read, one row
-  // address per tile).  The K operand read of a 16-lane group is 16
-  // consecutive rows of one chunk (256 contiguous bytes); the transposing V
-  // reads of a half-wave cover 128 bytes in each of two chunk columns, which
-  // the row flip on odd columns puts in opposite halves of the bank space.
-  const int kofs = 8 * (32 * grp + (col ^ (8 * (grp & 1))));  // + 1024 per MFMA step, + 128 per 16 keys
+  // address per tile).  The transposing V reads of a half-wave cover 128
+  // bytes in each of two chunk columns, which the row flip on odd columns
+  // puts in opposite halves of the bank space; the K operand reads pair
+  // their chunks to match (kperm above).
+  const int kofs = 8 * (32 * kperm + (col ^ (8 * (kperm & 1))));  // + 1024 per MFMA step, + 128 per 16 keys
   int vofs;                                                   // + 512 per 16 dv, + 128 for keys + 16
   {
     const int par = (col >> 1) & 1, key = 4 * grp + (col >> 2);
