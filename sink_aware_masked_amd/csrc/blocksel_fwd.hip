@@ -27,22 +27,26 @@ namespace bsel {
 constexpr int D = 128;
 constexpr int G = 4;            // query heads per kv head
 constexpr int BS = 64;          // key block size = query tile
-constexpr int NW = 4;           // waves per workgroup
-constexpr int NB_PER_WAVE = 4;  // 16-column blocks per wave (16 queries x 4 heads)
+constexpr int NW = 8;           // waves per workgroup (two per SIMD)
+constexpr int NB_PER_WAVE = 2;  // 16-column blocks per wave (8 queries x 4 heads)
 constexpr int NQC = D / 32;     // 4 Q^T fragments per column block
 constexpr int NDV = D / 16;     // 8 output blocks
 constexpr int RCH = D / 8;      // 16 16-byte chunks per row
 constexpr int TILE_EL = BS * D; // bf16 elements of one K (or V) block
-constexpr int LDPW = BS * RCH / 64 / NW;  // 4 direct-to-LDS loads per wave per tensor
+constexpr int LDPW = BS * RCH / 64 / NW;  // 2 direct-to-LDS loads per wave per tensor
 constexpr int MAXW = 32;        // selection words per query held in LDS per pass (1024 blocks)
 }  // namespace bsel
 
+// 8 waves of 8 queries x 4 heads each, held to 256 registers, so two waves
+// share every SIMD and one's softmax or LDS waits overlap the other's MFMAs.
 template <int SINK>
-__global__ __launch_bounds__(256) void blocksel_fwd_bf16(const Params p) {
+__global__ __launch_bounds__(64 * bsel::NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void blocksel_fwd_bf16(const Params p) {
   using namespace bsel;
-  __shared__ __attribute__((aligned(16))) bf16 kv0[2 * TILE_EL];  // stage = K block, V block
-  __shared__ __attribute__((aligned(16))) bf16 kv1[2 * TILE_EL];
-  __shared__ __attribute__((aligned(16))) bf16 kv2[2 * TILE_EL];
+  __shared__ __attribute__((aligned(16))) bf16 kvs[3 * 2 * TILE_EL];  // 3 stages of (K block, V block)
+  bf16* const kv0 = kvs;
+  bf16* const kv1 = kvs + 2 * TILE_EL;
+  bf16* const kv2 = kvs + 4 * TILE_EL;
   __shared__ uint32_t qbits[BS][MAXW];
   __shared__ uint32_t ubits[MAXW];
   __shared__ int blist[32 * MAXW];
@@ -74,7 +78,7 @@ __global__ __launch_bounds__(256) void blocksel_fwd_bf16(const Params p) {
   bf16x8 qf[NB_PER_WAVE][NQC];
 #pragma unroll
   for (int nb = 0; nb < NB_PER_WAVE; ++nb) {
-    qi[nb] = q0 + 16 * wave + 4 * nb + (col >> 2);
+    qi[nb] = q0 + 4 * NB_PER_WAVE * wave + 4 * nb + (col >> 2);
     const int qc = min(qi[nb], p.T - 1);
     dstart[nb] = __ldg(p.cu + find_segment(p.cu, p.num_seqs, qc));
     const bf16* qrow = qg + (int64_t)qc * p.q_row + (int64_t)h * p.q_head + 8 * grp;
@@ -132,7 +136,7 @@ __global__ __launch_bounds__(256) void blocksel_fwd_bf16(const Params p) {
     const bf16* vs = st + TILE_EL;
 #pragma unroll
     for (int nb = 0; nb < NB_PER_WAVE; ++nb) {
-      const int ql = 16 * wave + 4 * nb + (col >> 2);
+      const int ql = 4 * NB_PER_WAVE * wave + 4 * nb + (col >> 2);
       const bool sel = (qbits[ql][wsel] >> (blk & 31)) & 1u;
       if (__ballot(sel) == 0) continue;  // none of the 4 queries picked this block
       // is the whole block causal and inside the document for every column?
@@ -207,7 +211,7 @@ __global__ __launch_bounds__(256) void blocksel_fwd_bf16(const Params p) {
     // ---- selection bits of the 64 queries, 32 blocks per word; the 32 byte
     // loads of a word are independent (clamped index, masked bit)
     __syncthreads();  // the previous pass is done with qbits / blist / the ring
-    for (int t = tid; t < BS * nwords; t += 256) {
+    for (int t = tid; t < BS * nwords; t += 64 * NW) {
       const int q = t / nwords, w = t - q * nwords;
       uint32_t bits = 0;
       const int qrow_idx = q0 + q;
@@ -263,21 +267,39 @@ __global__ __launch_bounds__(256) void blocksel_fwd_bf16(const Params p) {
     }
   }
 
+  // ---- epilogue.  Each (query, head) output row is 256 contiguous bytes;
+  // the accumulators hold 4-element pieces of 16 such rows, so each wave
+  // stages its 8 queries x 4 heads in the (idle) ring, rows padded by 8
+  // elements, and stores them back 16 bytes per lane, whole lines.
   const float sink2 = (SINK == kSinkNull) ? __ldg(p.sinks + h) * kLog2e : 0.0f;
+  constexpr int OS = D + 8;
+  constexpr int ROWS = 4 * NB_PER_WAVE * G;  // (query, head) rows per wave
+  static_assert(NW * ROWS * OS <= 6 * TILE_EL, "staging fits the ring");
+  lds_barrier();  // every wave is done with the ring
+  bf16* ost = kvs + wave * ROWS * OS;
 #pragma unroll
   for (int nb = 0; nb < NB_PER_WAVE; ++nb) {
     const float l = sum_over_groups(lsum[nb]);
-    if (qi[nb] > qlast) continue;
     const float f = sink_fold<SINK>(m2[nb], l, sink2);
-    bf16* orow = static_cast<bf16*>(p.out) + (int64_t)qi[nb] * p.o_row + (int64_t)h * p.o_head + 4 * grp;
+    const int r = 4 * (4 * nb + (col >> 2)) + hh;  // row (query, head) of this lane
 #pragma unroll
     for (int n = 0; n < NDV; ++n) {
       bf16x4 o;
 #pragma unroll
       for (int e = 0; e < 4; ++e) o[e] = static_cast<bf16>(acc[nb][n][e] * f);
-      *reinterpret_cast<bf16x4*>(orow + 16 * n) = o;
+      *reinterpret_cast<bf16x4*>(ost + r * OS + 16 * n + 4 * grp) = o;
     }
-    if (grp == 0) p.lse[(int64_t)h * p.T + qi[nb]] = lse_natural(m2[nb], l);
+    if (grp == 0 && qi[nb] <= qlast) p.lse[(int64_t)h * p.T + qi[nb]] = lse_natural(m2[nb], l);
+  }
+  const int qw0 = q0 + 4 * NB_PER_WAVE * wave;
+#pragma unroll
+  for (int u = 0; u < ROWS * RCH / 64; ++u) {
+    const int c = lane + 64 * u;
+    const int r = c / RCH, cc = c - r * RCH;
+    const int qq = qw0 + (r >> 2), hd = kvh * G + (r & 3);
+    const bf16x8 v = *reinterpret_cast<const bf16x8*>(ost + r * OS + 8 * cc);
+    if (qq <= qlast)
+      *reinterpret_cast<bf16x8*>(static_cast<bf16*>(p.out) + (int64_t)qq * p.o_row + (int64_t)hd * p.o_head + 8 * cc) = v;
   }
 }
 
@@ -287,7 +309,7 @@ hipError_t launch_blocksel_bf16(const Params& p, int sink, hipStream_t st) {
     return hipErrorInvalidValue;
   Params q = p;
   q.num_tiles = (p.T + BS - 1) / BS;
-  const dim3 grid((unsigned)(q.num_tiles * p.Hkv)), block(256);
+  const dim3 grid((unsigned)(q.num_tiles * p.Hkv)), block(64 * NW);
   switch (sink) {
     case kSinkNone: hipLaunchKernelGGL((blocksel_fwd_bf16<kSinkNone>), grid, block, 0, st, q); break;
     case kSinkKey0: hipLaunchKernelGGL((blocksel_fwd_bf16<kSinkKey0>), grid, block, 0, st, q); break;
