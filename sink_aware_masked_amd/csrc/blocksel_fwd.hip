@@ -35,6 +35,8 @@ constexpr int RCH = D / 8;      // 16 16-byte chunks per row
 constexpr int TILE_EL = BS * D; // bf16 elements of one K (or V) block
 constexpr int LDPW = BS * RCH / 64 / NW;  // 2 direct-to-LDS loads per wave per tensor
 constexpr int MAXW = 32;        // selection words per query held in LDS per pass (1024 blocks)
+constexpr int NSTAGE = 4;       // LDS ring depth: three blocks in flight behind the one computed
+static_assert(NSTAGE >= 2 && NSTAGE <= 4, "the in-flight wait below covers up to two later blocks");
 }  // namespace bsel
 
 // 8 waves of 8 queries x 4 heads each, held to 256 registers, so two waves
@@ -43,10 +45,7 @@ template <int SINK>
 __global__ __launch_bounds__(64 * bsel::NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void blocksel_fwd_bf16(const Params p) {
   using namespace bsel;
-  __shared__ __attribute__((aligned(16))) bf16 kvs[3 * 2 * TILE_EL];  // 3 stages of (K block, V block)
-  bf16* const kv0 = kvs;
-  bf16* const kv1 = kvs + 2 * TILE_EL;
-  bf16* const kv2 = kvs + 4 * TILE_EL;
+  __shared__ __attribute__((aligned(16))) bf16 kvs[NSTAGE * 2 * TILE_EL];  // stages of (K block, V block)
   __shared__ uint32_t qbits[BS][MAXW];
   __shared__ uint32_t ubits[MAXW];
   __shared__ int blist[32 * MAXW];
@@ -228,42 +227,50 @@ void blocksel_fwd_bf16(const Params p) {
       qbits[q][w] = bits;
     }
     __syncthreads();
-    // union over the 64 queries, then the list of blocks to stage
-    if (tid < nwords) {
-      uint32_t u = 0;
-      for (int q = 0; q < BS; ++q) u |= qbits[q][tid];
-      ubits[tid] = u;
+    // union over the 64 queries (a wave per word, OR-reduced across lanes),
+    // then the list of blocks to stage (one wave: prefix sum of the words'
+    // popcounts, each lane writing its word's blocks)
+    for (int w = wave; w < nwords; w += NW) {
+      uint32_t u = qbits[lane][w];
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) u |= (uint32_t)__shfl_xor((int)u, off);
+      if (lane == 0) ubits[w] = u;
     }
     __syncthreads();
-    if (tid == 0) {
-      int n = 0;
-      for (int w = 0; w < nwords; ++w) {
-        uint32_t pending = ubits[w];
-        while (pending) {
-          blist[n++] = 32 * (wb + w) + __builtin_ctz(pending);
-          pending &= pending - 1;
-        }
+    if (wave == 0) {
+      const uint32_t bits = lane < nwords ? ubits[lane] : 0u;
+      const int cnt = __builtin_popcount(bits);
+      int x = cnt;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(x, off);
+        if (lane >= off) x += y;
       }
-      nblist = n;
+      int n = x - cnt;
+      uint32_t pending = bits;
+      while (pending) {
+        blist[n++] = 32 * (wb + lane) + __builtin_ctz(pending);
+        pending &= pending - 1;
+      }
+      if (lane == 63) nblist = x;
     }
     __syncthreads();
     const int nbl = nblist;
 
-    // block bi lives in stage bi % 3; the loop is unrolled by the ring depth
-    // so every stage is a compile-time LDS array
-    auto step = [&](int bi, bf16* cur, bf16* ahead2) {
-      if (bi + 1 < nbl) wait_vmcnt<2 * LDPW>(); else wait_vmcnt<0>();
+    // block bi lives in stage bi % NSTAGE; NSTAGE - 1 blocks are in flight
+    // behind the one being computed
+#pragma unroll
+    for (int u = 0; u < NSTAGE - 1; ++u)
+      if (u < nbl) issue(blist[u], kvs + u * 2 * TILE_EL);
+    for (int bi = 0; bi < nbl; ++bi) {
+      const int ahead = min(NSTAGE - 2, nbl - 1 - bi);  // later blocks allowed in flight
+      if (ahead >= 2) wait_vmcnt<4 * LDPW>();
+      else if (ahead == 1) wait_vmcnt<2 * LDPW>();
+      else wait_vmcnt<0>();
       lds_barrier();  // block bi is in LDS for every wave; block bi-1's stage is free
-      if (bi + 2 < nbl) issue(blist[bi + 2], ahead2);
+      if (bi + NSTAGE - 1 < nbl) issue(blist[bi + NSTAGE - 1], kvs + ((bi + NSTAGE - 1) % NSTAGE) * 2 * TILE_EL);
       const int blk = blist[bi];
-      compute(blk, (blk >> 5) - wb, cur);
-    };
-    if (nbl > 0) issue(blist[0], kv0);
-    if (nbl > 1) issue(blist[1], kv1);
-    for (int bi = 0; bi < nbl; bi += 3) {
-      step(bi, kv0, kv2);
-      if (bi + 1 < nbl) step(bi + 1, kv1, kv0);
-      if (bi + 2 < nbl) step(bi + 2, kv2, kv1);
+      compute(blk, (blk >> 5) - wb, kvs + (bi % NSTAGE) * 2 * TILE_EL);
     }
   }
 
@@ -274,7 +281,7 @@ void blocksel_fwd_bf16(const Params p) {
   const float sink2 = (SINK == kSinkNull) ? __ldg(p.sinks + h) * kLog2e : 0.0f;
   constexpr int OS = D + 8;
   constexpr int ROWS = 4 * NB_PER_WAVE * G;  // (query, head) rows per wave
-  static_assert(NW * ROWS * OS <= 6 * TILE_EL, "staging fits the ring");
+  static_assert(NW * ROWS * OS <= NSTAGE * 2 * TILE_EL, "staging fits the ring");
   lds_barrier();  // every wave is done with the ring
   bf16* ost = kvs + wave * ROWS * OS;
 #pragma unroll
