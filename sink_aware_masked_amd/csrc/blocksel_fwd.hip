@@ -85,6 +85,10 @@ void blocksel_fwd_bf16(const Params p) {
     for (int c = 0; c < NQC; ++c) {
       qf[nb][c] = *reinterpret_cast<const bf16x8*>(qrow + 32 * c);
       if (qi[nb] > qlast) qf[nb][c] = bf16x8{};
+      if (p.scale_log2 < 0.0f) {  // move a negative scale into Q's sign (exact)
+        typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4;
+        qf[nb][c] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, qf[nb][c]) ^ 0x80008000u);
+      }
     }
   }
 
@@ -101,7 +105,10 @@ void blocksel_fwd_bf16(const Params p) {
 #pragma unroll
   for (int n = 0; n < NDV; ++n) voff[n] = vrow + 8 * ((2 * n + ((col >> 1) & 1)) ^ vfr);
 
-  const float sl2 = p.scale_log2;
+  // sl2 > 0 from here on (a negative scale sits in Q's sign; a zero scale
+  // becomes the least normal float, which leaves every finite logit within
+  // 2^-100 of zero, so its exp2 rounds to 1 as for the exact zero logits)
+  const float sl2 = fmaxf(fabsf(p.scale_log2), __FLT_MIN__);
   const float bias2 = (SINK == kSinkKey0) ? __ldg(p.sinks + h) * kLog2e : 0.0f;
   float m2[NB_PER_WAVE], lsum[NB_PER_WAVE];
   floatx4 acc[NB_PER_WAVE][NDV];
@@ -144,6 +151,9 @@ void blocksel_fwd_bf16(const Params p) {
       const bool has_key0 =
           SINK == kSinkKey0 && __ballot(sel & (dstart[nb] >= kb0) & (dstart[nb] < kb0 + BS)) != 0;
 
+      // s keeps the raw dot products (unselected / masked ones -inf); the
+      // scale, the key-0 bias and the reference max go into one fma in the
+      // exponent, so a zero bias gives bit for bit the no-sink numbers
       float s[4][4];
 #pragma unroll
       for (int sb = 0; sb < 4; ++sb) {
@@ -153,19 +163,37 @@ void blocksel_fwd_bf16(const Params p) {
         for (int cc = 0; cc < NQC; ++cc)
           a = mfma32(*reinterpret_cast<const bf16x8*>(krow + koff[cc]), qf[nb][cc], a);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int j = kb0 + 16 * sb + 4 * grp + e;
-          float x = a[e] * sl2;
-          if (has_key0) x += (j == dstart[nb]) ? bias2 : 0.0f;
-          const bool ok = edge ? (sel & (j <= qi[nb]) & (j >= dstart[nb])) : sel;
-          s[sb][e] = ok ? x : kNegInf;
-        }
+        for (int e = 0; e < 4; ++e) s[sb][e] = a[e];
       }
+      if (edge) {  // wave-uniform: some selected column sees causality or a document start
+#pragma unroll
+        for (int sb = 0; sb < 4; ++sb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int j = kb0 + 16 * sb + 4 * grp + e;
+            s[sb][e] = (sel & (j <= qi[nb]) & (j >= dstart[nb])) ? s[sb][e] : kNegInf;
+          }
+      } else {
+#pragma unroll
+        for (int sb = 0; sb < 4; ++sb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) s[sb][e] = sel ? s[sb][e] : kNegInf;
+      }
+      const int dk = dstart[nb] - kb0 - 4 * grp;  // key-0 column of this lane, as 16 sb + e
       float mt = kNegInf;
+      if (has_key0) {
 #pragma unroll
-      for (int sb = 0; sb < 4; ++sb)
+        for (int sb = 0; sb < 4; ++sb)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) mt = fmaxf(mt, s[sb][e]);
+          for (int e = 0; e < 4; ++e)
+            mt = fmaxf(mt, __builtin_fmaf(s[sb][e], sl2, (16 * sb + e == dk) ? bias2 : 0.0f));
+      } else {
+#pragma unroll
+        for (int sb = 0; sb < 4; ++sb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) mt = fmaxf(mt, s[sb][e]);
+        mt *= sl2;  // sl2 > 0: the max commutes with the scaling
+      }
       mt = max_over_groups(mt);
       if (__ballot(mt > m2[nb] + kRescaleLog2) != 0) {  // lazy rescale (wave-uniform)
         const float mn = fmaxf(m2[nb], mt);
@@ -177,13 +205,24 @@ void blocksel_fwd_bf16(const Params p) {
       }
       const float mu = (m2[nb] == kNegInf) ? 0.0f : m2[nb];
       float ps = 0.0f;
+      if (has_key0) {
+        const float bmu = bias2 - mu;
 #pragma unroll
-      for (int sb = 0; sb < 4; ++sb)
+        for (int sb = 0; sb < 4; ++sb)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          s[sb][e] = exp2f_fast(s[sb][e] - mu);
-          ps += s[sb][e];
-        }
+          for (int e = 0; e < 4; ++e) {
+            s[sb][e] = exp2f_fast(__builtin_fmaf(s[sb][e], sl2, (16 * sb + e == dk) ? bmu : -mu));
+            ps += s[sb][e];
+          }
+      } else {
+#pragma unroll
+        for (int sb = 0; sb < 4; ++sb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            s[sb][e] = exp2f_fast(__builtin_fmaf(s[sb][e], sl2, -mu));
+            ps += s[sb][e];
+          }
+      }
       lsum[nb] += ps;
 #pragma unroll
       for (int c2 = 0; c2 < 2; ++c2) {
