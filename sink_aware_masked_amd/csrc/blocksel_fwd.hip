@@ -63,7 +63,8 @@ void blocksel_fwd_bf16(const Params p) {
 
   // candidate key blocks: from the document start of the first query to the
   // query block itself
-  const int blo = __ldg(p.cu + find_segment(p.cu, p.num_seqs, q0)) / BS;
+  const SegWindow sg = seg_window(p.cu, p.num_seqs, q0, qlast);  // documents of the tile
+  const int blo = sg.bound(p.cu, sg.sa) / BS;
   const int bhi = qlast / BS;
   const uint8_t* tab = p.bsel + (int64_t)hidx * p.bsel_head;
 
@@ -79,7 +80,11 @@ void blocksel_fwd_bf16(const Params p) {
   for (int nb = 0; nb < NB_PER_WAVE; ++nb) {
     qi[nb] = q0 + 4 * NB_PER_WAVE * wave + 4 * nb + (col >> 2);
     const int qc = min(qi[nb], p.T - 1);
-    dstart[nb] = __ldg(p.cu + find_segment(p.cu, p.num_seqs, qc));
+    dstart[nb] = 0;
+    for (int s2 = sg.sa; s2 <= sg.sb; ++s2) {
+      const int cs = sg.bound(p.cu, s2);
+      if (qc >= cs) dstart[nb] = cs;  // last document start at or before qc
+    }
     const bf16* qrow = qg + (int64_t)qc * p.q_row + (int64_t)h * p.q_head + 8 * grp;
 #pragma unroll
     for (int c = 0; c < NQC; ++c) {

@@ -181,6 +181,50 @@ __device__ __forceinline__ int find_segment(const int32_t* __restrict__ cu, int 
   return lo;
 }
 
+// Segment lookups with few dependent loads.  A chain of dependent global
+// loads costs a full memory latency per link at kernel start, when every
+// workgroup issues its first loads at once, so the lookups below keep the
+// chain at one or two vector loads.
+//
+// Largest s in [0, num_seqs) with cu[s] <= t, for a wave-uniform t (the whole
+// wave calls it): a 64-ary search, each level one vector load of 64 evenly
+// spaced entries and a ballot (cu is non-decreasing, so the lanes with
+// cu <= t form a prefix).  num_seqs <= 64 costs one load, <= 4096 two.
+__device__ __forceinline__ int find_segment_w(const int32_t* __restrict__ cu, int num_seqs, int t) {
+  const int lane = threadIdx.x & 63;
+  int lo = 0, n = num_seqs;  // invariant: cu[lo] <= t, answer in [lo, lo + n)
+  while (n > 64) {
+    const int step = (n + 63) >> 6;
+    const int j = lane * step;
+    const int v = j < n ? __ldg(cu + lo + j) : 0x7fffffff;
+    const int k = 63 - __builtin_clzll(__ballot(v <= t));
+    lo += k * step;
+    n = min(step, n - k * step);
+  }
+  const int v = lane < n ? __ldg(cu + lo + lane) : 0x7fffffff;
+  return lo + 63 - __builtin_clzll(__ballot(v <= t));
+}
+
+// The segments that rows [r0, r1] (wave-uniform) fall in: sa .. sb, with the
+// boundaries cu[sa .. sa + 63] held one per lane, read back by readlane.
+struct SegWindow {
+  int sa, sb, v;  // v = cu[min(sa + lane, num_seqs)]
+  // cu[s] for a wave-uniform s >= sa
+  __device__ __forceinline__ int bound(const int32_t* __restrict__ cu, int s) const {
+    const int j = s - sa;
+    return j < 64 ? __builtin_amdgcn_readlane(v, j) : __ldg(cu + s);
+  }
+};
+__device__ __forceinline__ SegWindow seg_window(const int32_t* __restrict__ cu, int num_seqs, int r0, int r1) {
+  SegWindow w;
+  const int lane = threadIdx.x & 63;
+  w.sa = find_segment_w(cu, num_seqs, r0);
+  w.v = __ldg(cu + min(w.sa + lane, num_seqs));
+  const int k = 63 - __builtin_clzll(__ballot((w.sa + lane < num_seqs) & (w.v <= r1)));
+  w.sb = k < 63 ? w.sa + k : find_segment_w(cu, num_seqs, r1);
+  return w;
+}
+
 // Blocks are dispatched round-robin over the 8 XCDs (block b -> XCD b % 8).
 // Renumber so that each XCD receives one contiguous range of logical blocks:
 // neighbouring tiles, which read overlapping K/V rows, then share an L2.
