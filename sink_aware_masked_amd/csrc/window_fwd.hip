@@ -8,8 +8,7 @@
 // of 32 rows.  The key band of the workgroup, [lo(first row), hi(last row)],
 // streams through LDS slots, 64 keys (K tile then V tile) per slot, filled by
 // direct-to-LDS loads a round of slots at a time: with a 64-key window the
-// whole band (256 keys) is one round, in flight at once, and the blocks of
-// its middle tiles start as soon as those have landed.  Q goes straight to
+// whole band (256 keys) is one round, in flight at once.  Q goes straight to
 // VGPRs.  Per wave and 32-key block:
 //   S^T[key][row] = K[key][:] . Q[row][:]          (MFMA 32x32x16 bf16)
 // so every lane owns one query row and 16 of the block's keys; masking is two
@@ -116,16 +115,16 @@ void window_fwd_bf16(const Params p) {
   const int r0w = r0 + 32 * wave;
   const bool wave_active = r0w <= rlast;
 
-  // ---- windows.  Sequences touching this tile: sg.sa .. sg.sb, their
-  // boundaries in a wave register (two dependent loads in all; all of them
-  // complete before the ring is in flight).
-  const SegWindow sg = seg_window(p.cu, p.num_seqs, r0, rlast);
-  const int kmin = max(sg.bound(p.cu, sg.sa), r0 - p.window);
-  const int kmax = min(sg.bound(p.cu, sg.sb + 1) - 1, rlast + p.window);
+  // ---- windows.  Sequences touching this tile: sa .. sb (scalar loads only,
+  // so no vector load is pending once the ring is in flight).
+  const int sa = find_segment(p.cu, p.num_seqs, r0);
+  const int sb = find_segment(p.cu, p.num_seqs, rlast);
+  const int kmin = max(__ldg(p.cu + sa), r0 - p.window);
+  const int kmax = min(__ldg(p.cu + sb + 1) - 1, rlast + p.window);
   const int ri = min(r0w + n, rlast);  // this lane's row (clamped past the end)
   int start = 0, end = 1;
-  for (int s = sg.sa; s <= sg.sb; ++s) {
-    const int cs = sg.bound(p.cu, s), ce = sg.bound(p.cu, s + 1);
+  for (int s = sa; s <= sb; ++s) {
+    const int cs = __ldg(p.cu + s), ce = __ldg(p.cu + s + 1);
     if (ri >= cs && ri < ce) { start = cs; end = ce; }
   }
   const int lo = max(start, ri - p.window);
@@ -178,22 +177,13 @@ void window_fwd_bf16(const Params p) {
     }
   };
   // Q^T fragments (B operand) straight to VGPRs: lane (n, hf) holds row
-  // r0w + n, dims 16 d + 8 hf + [0, 8).  Loaded by inline assembly: the
-  // compiler does not count these loads, so it inserts no wait for them that
-  // would also drain the tile loads issued behind them; the first tile wait
-  // (loads complete in issue order) releases them, and settle_q() then hands
-  // the registers back to the compiler.
+  // r0w + n, dims 16 d + 8 hf + [0, 8).
   bf16x8 qf[C::NQK];
   {
-    const char* qr = qg + (int64_t)min(r0w + n, rlast) * qrow + 16 * hf;
+    const char* qr = qg + (int64_t)min(r0w + n, rlast) * qrow;
 #pragma unroll
-    for (int d = 0; d < C::NQK; ++d)
-      asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(qf[d]) : "v"(qr + 32 * d) : "memory");
+    for (int d = 0; d < C::NQK; ++d) qf[d] = *reinterpret_cast<const bf16x8*>(qr + 32 * d + 16 * hf);
   }
-  auto settle_q = [&]() {  // after a vmcnt wait that covers the Q loads
-#pragma unroll
-    for (int d = 0; d < C::NQK; ++d) asm volatile("" : "+v"(qf[d]));
-  };
   // ---- per-lane LDS read offsets (bytes, relative to a slot)
   constexpr int KSTEP = C::ILV ? 2 : 1;
   const int kr = (n & ~7) | key_in8<D>(n & 7);  // K row of MFMA row n in a 32-key block
@@ -319,45 +309,29 @@ void window_fwd_bf16(const Params p) {
   };
 
   // ---- key loop, in rounds of NS tiles.  A round's tiles are all issued at
-  // once, middle tiles first: every wave's band covers the middle of the
-  // round, so after the first half of the round has landed (one wait, one
-  // barrier) each wave has work while the outer tiles are still arriving;
-  // after the second wait and barrier it finishes the round.  Between the two
-  // points no wave waits for another.  (A 64-key window on 128 rows is one
-  // round of 4 tiles: tiles 1, 2 hold 3 of each wave's 5 blocks.)
-  auto ord = [](int k, int n) {  // k-th tile of an n-tile round: middle first
-    const int m = (n - 1) >> 1;
-    return m + ((k & 1) ? (k + 1) >> 1 : -(k >> 1));
-  };
+  // once; after one wait and one barrier every wave runs through its blocks
+  // of the round without further synchronisation, so no wave waits at a
+  // barrier for another wave's share of a tile it does not need itself.
+  // (A 64-key window on 128 rows is one round.)
+  bool first = true;
   for (int t0 = 0; t0 < ntiles; t0 += C::NS) {
-    const int nr = min(C::NS, ntiles - t0);
-    const int split = (nr + 1) >> 1;
-    if (t0 > 0) lds_barrier();  // the previous round's slots are free
+    if (!first) lds_barrier();  // the previous round's slots are free
 #pragma unroll
-    for (int k = 0; k < C::NS; ++k)
-      if (k < nr) issue(t0 + ord(k, nr), ord(k, nr));
-    wait_tiles<C::NPW>(nr - split);
+    for (int u = 0; u < C::NS; ++u)
+      if (t0 + u < ntiles) issue(t0 + u, u);
+    wait_vmcnt<0>();
     lds_barrier();
-    if (t0 == 0) {
-      settle_q();
-      if (neg_scale) {
+    if (first && neg_scale) {
 #pragma unroll
-        for (int d = 0; d < C::NQK; ++d) {
-          typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4;
-          qf[d] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, qf[d]) ^ 0x80008000u);
-        }
+      for (int d = 0; d < C::NQK; ++d) {
+        typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4;
+        qf[d] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, qf[d]) ^ 0x80008000u);
       }
     }
+    first = false;
 #pragma unroll
-    for (int k = 0; k < C::NS; ++k)
-      if (k < split) compute(t0 + ord(k, nr), ord(k, nr));
-    if (nr > split) {
-      wait_vmcnt<0>();
-      lds_barrier();
-#pragma unroll
-      for (int k = 0; k < C::NS; ++k)
-        if (k >= split && k < nr) compute(t0 + ord(k, nr), ord(k, nr));
-    }
+    for (int u = 0; u < C::NS; ++u)
+      if (t0 + u < ntiles) compute(t0 + u, u);
   }
 
   // ---- epilogue.  O^T leaves the accumulators as 4-element pieces of 32
