@@ -301,20 +301,29 @@ void blocksel_fwd_bf16(const Params p) {
     __syncthreads();
     const int nbl = nblist;
 
-    // block bi lives in stage bi % NSTAGE; NSTAGE - 1 blocks are in flight
-    // behind the one being computed
+    // Blocks go in pairs: pair r lives in stages 2 (r % 2) and + 1.  One
+    // wait and one barrier per pair: pair r has landed for every wave, and
+    // every wave is done with pair r - 1, whose stages then take pair r + 1
+    // while pair r is computed.  Between barriers a wave runs through both
+    // blocks, so a wave whose queries chose neither block of a pair costs the
+    // others one barrier instead of two.
+    const int npair = (nbl + 1) >> 1;
+    auto issue_pair = [&](int r) {
 #pragma unroll
-    for (int u = 0; u < NSTAGE - 1; ++u)
-      if (u < nbl) issue(blist[u], kvs + u * 2 * TILE_EL);
-    for (int bi = 0; bi < nbl; ++bi) {
-      const int ahead = min(NSTAGE - 2, nbl - 1 - bi);  // later blocks allowed in flight
-      if (ahead >= 2) wait_vmcnt<4 * LDPW>();
-      else if (ahead == 1) wait_vmcnt<2 * LDPW>();
-      else wait_vmcnt<0>();
-      lds_barrier();  // block bi is in LDS for every wave; block bi-1's stage is free
-      if (bi + NSTAGE - 1 < nbl) issue(blist[bi + NSTAGE - 1], kvs + ((bi + NSTAGE - 1) % NSTAGE) * 2 * TILE_EL);
-      const int blk = blist[bi];
-      compute(blk, (blk >> 5) - wb, kvs + (bi % NSTAGE) * 2 * TILE_EL);
+      for (int u = 0; u < 2; ++u)
+        if (2 * r + u < nbl) issue(blist[2 * r + u], kvs + ((r & 1) * 2 + u) * 2 * TILE_EL);
+    };
+    issue_pair(0);
+    for (int r = 0; r < npair; ++r) {
+      wait_vmcnt<0>();
+      lds_barrier();
+      if (r + 1 < npair) issue_pair(r + 1);
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        if (2 * r + u < nbl) {
+          const int blk = blist[2 * r + u];
+          compute(blk, (blk >> 5) - wb, kvs + ((r & 1) * 2 + u) * 2 * TILE_EL);
+        }
     }
   }
 
