@@ -14,7 +14,7 @@
 // costs one pass over the list and no key tiles.  Key tiles of 32 gathered
 // rows go straight from memory into a 2-stage LDS ring (direct-to-LDS loads,
 // the next tile in flight behind the one being computed, waited for explicitly),
-// stored chunk-major so both operand reads below are free of bank conflicts.
+// stored line-major (below) so both operand reads are free of bank conflicts.
 // Per tile and wave:
 //   S^T[key][head] = K[key][:576] . Q[head][:576]   (18 MFMA 16x16x32 per 16 keys;
 //                                                   Q of the wave's 16 heads in VGPRs)
@@ -64,39 +64,36 @@ void topk_mla_fwd_bf16(const Params p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   const int col = lane & 15, grp = lane >> 4;
   const int h = hg * HPB + wave * HPW + col;  // this lane's head
-  // 16-byte chunk (of 4 per 32 dims) that k-slot grp carries in the S^T
-  // MFMAs: groups 0, 1 take the even chunks and 2, 3 the odd ones, so the
-  // lanes that one pass of a 16-byte LDS read serves (lanes 0-7 with 24-31,
-  // 8-15 with 16-23, and the same in the upper half) see the same row flip
-  // (below) and land in opposite halves of the bank space
-  const int kperm = ((grp & 1) << 1) | (grp >> 1);
 
   const bf16* qg = static_cast<const bf16*>(p.q);
   const bf16* kg = static_cast<const bf16*>(p.k);
   bf16x8 qf[NQC];
   {
-    // k-slot grp of each MFMA step holds dims 32 c + 8 kperm + [0, 8); the
-    // same permutation on the K side (below) keeps the two operands in step
-    const bf16* qrow = qg + (int64_t)i * p.q_row + (int64_t)h * p.q_head + 8 * kperm;
+    const bf16* qrow = qg + (int64_t)i * p.q_row + (int64_t)h * p.q_head + 8 * grp;
 #pragma unroll
     for (int c = 0; c < NQC; ++c) qf[c] = *reinterpret_cast<const bf16x8*>(qrow + 32 * c);
   }
 
-  // Tile layout in LDS, chunk-major: 16-byte chunk c (dims 8c .. 8c+7) of
-  // tile row r sits at element 8 * (32 c + (r ^ 8 (c & 1))).  One 1-KB
-  // direct-to-LDS load then fills two chunk columns of all 32 rows, so a lane
-  // gathers the same row for every load of a tile (one index read, one row
-  // address per tile).  The transposing V reads of a half-wave cover 128
-  // bytes in each of two chunk columns, which the row flip on odd columns
-  // puts in opposite halves of the bank space; the K operand reads pair
-  // their chunks to match (kperm above).
-  const int kofs = 8 * (32 * kperm + (col ^ (8 * (kperm & 1))));  // + 1024 per MFMA step, + 128 per 16 keys
-  int vofs;                                                   // + 512 per 16 dv, + 128 for keys + 16
+  // Tile layout in LDS, line-major: tile row r = 8 g + rr (g = 0..3) and
+  // 16-byte chunk c = 8 L + c8 (L = 0..8, one 128-byte line of the row) sit
+  // at byte (4 L + g) * 1024 + 128 rr + 16 (c8 ^ rr).  One 1-KB direct-to-LDS
+  // load then fills one line of 8 rows, so each load instruction touches 8
+  // whole cache lines (32 B pieces of 32 lines in a chunk-major layout cost
+  // 15 % more time at issue), and wave g gathers rows 8 g .. 8 g + 7 — one
+  // row per lane, one index read per tile.  The XOR puts the 8 rows of a
+  // 16-byte operand read pass (and the 8 rows x 2 chunks of a transposing
+  // read pass) in distinct bank groups.
+  const int rrk = col & 7;  // K operand row in its group of 8
+  const int kofs_e = ((col >> 3) * 1024 + 128 * rrk + 16 * ((grp ^ rrk) & 7)) / 2;        // even MFMA step
+  const int kofs_o = ((col >> 3) * 1024 + 128 * rrk + 16 * (((4 + grp) ^ rrk) & 7)) / 2;  // odd MFMA step
+  // (elements; + 2048 per pair of MFMA steps = one line, + 1024 per 16 keys)
+  int vofs4[4];  // V^T reads, by output block n % 4; + 2048 per 4 blocks, + 1024 for keys + 16
   {
-    const int par = (col >> 1) & 1, key = 4 * grp + (col >> 2);
-    vofs = 8 * (32 * par + (key ^ (8 * par))) + 4 * (col & 1);
+    const int rrv = 4 * (grp & 1) + (col >> 2), gv = grp >> 1, par = (col >> 1) & 1;
+#pragma unroll
+    for (int n4 = 0; n4 < 4; ++n4)
+      vofs4[n4] = (gv * 1024 + 128 * rrv + 16 * (((2 * n4 + par) ^ rrv) & 7) + 8 * (col & 1)) / 2;
   }
-  const int drow = (lane & 31) ^ (8 * (lane >> 5));  // tile row this lane gathers
 
   const float sl2 = p.scale_log2;
   float m2 = kNegInf, lsum = 0.0f;
@@ -143,13 +140,12 @@ void topk_mla_fwd_bf16(const Params p) {
     // masked to -inf, so they carry zero weight).
     const int ntiles = (nvalid + KT - 1) / KT;
     auto issue = [&](int t, bf16* st) {
-      const uint32_t st_addr = lds_addr(st) + (uint32_t)(wave * LDPW * 1024);
-      // load u of this wave fills chunk columns 2 (wave LDPW + u) and + 1
-      const int posr = t * KT + drow;
+      // load u of wave w fills line u of rows 8 w .. 8 w + 7 (1 KB block 4 u + w)
+      const int posr = t * KT + 8 * wave + (lane >> 3);
       const int j = kidx[posr < nvalid ? posr : 0];
-      const bf16* g = kg + (int64_t)j * p.k_row + 8 * (lane >> 5) + 16 * LDPW * wave;
+      const bf16* g = kg + (int64_t)j * p.k_row + 8 * ((lane & 7) ^ (lane >> 3));
 #pragma unroll
-      for (int u = 0; u < LDPW; ++u) load_lds16_m0(g + 16 * u, st_addr + u * 1024);
+      for (int u = 0; u < LDPW; ++u) load_lds16_m0(g + 64 * u, lds_addr(st) + (4 * u + wave) * 1024);
     };
 
     // ---- one tile: S, online softmax with lazy rescale, PV
@@ -159,15 +155,17 @@ void topk_mla_fwd_bf16(const Params p) {
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb) {
         floatx4 a = {0.f, 0.f, 0.f, 0.f};
-        const bf16* krow = st + kofs + 128 * sb;
+        const bf16* krow = st + 1024 * sb;
         bf16x8 kb[KPIPE];
 #pragma unroll
-        for (int cc = 0; cc < KPIPE; ++cc) kb[cc] = *reinterpret_cast<const bf16x8*>(krow + 1024 * cc);
+        for (int cc = 0; cc < KPIPE; ++cc)
+          kb[cc] = *reinterpret_cast<const bf16x8*>(krow + ((cc & 1) ? kofs_o : kofs_e) + 2048 * (cc >> 1));
 #pragma unroll
         for (int cc = 0; cc < NQC; ++cc) {
           a = mfma32(kb[cc % KPIPE], qf[cc], a);
           const int nx = cc + KPIPE;
-          if (nx < NQC) kb[cc % KPIPE] = *reinterpret_cast<const bf16x8*>(krow + 1024 * nx);
+          if (nx < NQC)
+            kb[cc % KPIPE] = *reinterpret_cast<const bf16x8*>(krow + ((nx & 1) ? kofs_o : kofs_e) + 2048 * (nx >> 1));
         }
         const bool all_in = t0 + 16 * sb + 4 * grp + 3 < nvalid;
 #pragma unroll
@@ -202,8 +200,8 @@ void topk_mla_fwd_bf16(const Params p) {
       lsum += ps;
       // V^T operands run VPIPE blocks ahead of the MFMAs that use them
       auto vload = [&](int n) {
-        const bf16* v0 = st + vofs + 512 * n;
-        return cat8(lds_read_tr4(v0), lds_read_tr4(v0 + 128));
+        const bf16* v0 = st + vofs4[n & 3] + 2048 * (n >> 2);
+        return cat8(lds_read_tr4(v0), lds_read_tr4(v0 + 1024));
       };
       bf16x8 vb[VPIPE];
 #pragma unroll
