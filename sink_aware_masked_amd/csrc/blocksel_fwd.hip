@@ -9,9 +9,12 @@
 // per-query bit masks in LDS (64-bit table offsets), and their union decides
 // which key blocks are staged at all: each selected block is loaded once into
 // LDS and shared by all 64 queries x 4 heads.  Blocks go straight from memory
-// into a 3-stage LDS ring (direct-to-LDS loads; two blocks in flight behind
-// the one being computed), K and V row-major with a 16-byte chunk swizzle so
-// the operand reads are free of bank conflicts.  MFMA columns are
+// into a 4-stage LDS ring (direct-to-LDS loads, two blocks at a time), stored
+// line-major: row r = 8 g + rr and 16-byte chunk c = 8 L + c8 (L = which
+// 128-byte half of the row) sit at byte (8 L + g) * 1024 + 128 rr +
+// 16 (c8 ^ rr).  One 1-KB load instruction then fills one line of 8 rows, and
+// both the 16-byte K operand reads (16 rows at one chunk) and the transposing
+// V reads (8 rows x 32 bytes per half-wave) fall on distinct banks.  MFMA columns are
 // (query, head) pairs: a 16-column block holds 4 queries x their 4 heads, so
 // the 4 heads of a query -- which share one selection -- fill the MFMA's N
 // dimension.  Per 16-column block the wave skips a staged key block unless one
@@ -97,18 +100,20 @@ void blocksel_fwd_bf16(const Params p) {
     }
   }
 
-  // Per-lane LDS element offsets within a block (see swz16): K operand rows
-  // 16*sb + col, chunks 4*cc + grp; V^T rows 32*c2 + 4*grp + col/4 (+16),
-  // chunk pairs 2n, 2n+1.
-  const int kfr = swz16(col);
+  // Per-lane LDS element offsets within a block (line-major layout above):
+  // K operand rows 16*sb + col (+1024 elements per sb), chunks 4*cc + grp;
+  // V^T rows 32*c2 + 4*grp + col/4 (+2048 per c2, +1024 for the second 16
+  // keys), chunk pair 2n, 2n+1 of dv block n.
+  const int rk = col & 7;
   int koff[NQC];
 #pragma unroll
-  for (int cc = 0; cc < NQC; ++cc) koff[cc] = col * D + 8 * ((4 * cc + grp) ^ kfr);
-  const int vfr = ((col >> 2) << 1) | (grp & 1);
-  const int vrow = (4 * grp + (col >> 2)) * D + 4 * (col & 1);
+  for (int cc = 0; cc < NQC; ++cc)
+    koff[cc] = ((cc >> 1) * 8 + (col >> 3)) * 512 + 64 * rk + 8 * (((4 * (cc & 1) + grp) ^ rk) & 7);
+  const int rv = 4 * (grp & 1) + (col >> 2), par = (col >> 1) & 1;
   int voff[NDV];
 #pragma unroll
-  for (int n = 0; n < NDV; ++n) voff[n] = vrow + 8 * ((2 * n + ((col >> 1) & 1)) ^ vfr);
+  for (int n = 0; n < NDV; ++n)
+    voff[n] = (n >> 2) * 4096 + (grp >> 1) * 512 + 64 * rv + 8 * (((2 * (n & 3) + par) ^ rv) & 7) + 4 * (col & 1);
 
   // sl2 > 0 from here on (a negative scale sits in Q's sign; a zero scale
   // becomes the least normal float, which leaves every finite logit within
@@ -131,10 +136,10 @@ void blocksel_fwd_bf16(const Params p) {
     const uint32_t base = lds_addr(st) + (uint32_t)(wave * LDPW * 1024);
 #pragma unroll
     for (int u = 0; u < LDPW; ++u) {
-      const int ch = (wave * LDPW + u) * 64 + lane;
-      const int r = ch / RCH, cc = ch - r * RCH;
+      const int i = wave * LDPW + u;  // 1-KB piece: line i >> 3 of rows 8 (i & 7) .. + 7
+      const int r = 8 * (i & 7) + (lane >> 3);
       const int j = min(blk * BS + r, p.T - 1);
-      const int c = 8 * (cc ^ swz16(r));
+      const int c = 8 * (8 * (i >> 3) + ((lane & 7) ^ (lane >> 3)));
       load_lds16_m0(kg + (int64_t)j * p.k_row + c, base + u * 1024);
       load_lds16_m0(vg + (int64_t)j * p.v_row + c, base + TILE_EL * 2 + u * 1024);
     }
@@ -163,7 +168,7 @@ void blocksel_fwd_bf16(const Params p) {
 #pragma unroll
       for (int sb = 0; sb < 4; ++sb) {
         floatx4 a = {0.f, 0.f, 0.f, 0.f};
-        const bf16* krow = ks + sb * 16 * D;
+        const bf16* krow = ks + sb * 1024;
 #pragma unroll
         for (int cc = 0; cc < NQC; ++cc)
           a = mfma32(*reinterpret_cast<const bf16x8*>(krow + koff[cc]), qf[nb][cc], a);
@@ -237,10 +242,10 @@ void blocksel_fwd_bf16(const Params p) {
           pb[e] = static_cast<bf16>(s[2 * c2][e]);
           pb[4 + e] = static_cast<bf16>(s[2 * c2 + 1][e]);
         }
-        const bf16* v0 = vs + c2 * 32 * D;
+        const bf16* v0 = vs + c2 * 2048;
 #pragma unroll
         for (int n = 0; n < NDV; ++n) {
-          const bf16x8 va = cat8(lds_read_tr4(v0 + voff[n]), lds_read_tr4(v0 + 16 * D + voff[n]));
+          const bf16x8 va = cat8(lds_read_tr4(v0 + voff[n]), lds_read_tr4(v0 + 1024 + voff[n]));
           acc[nb][n] = mfma32(va, pb, acc[nb][n]);
         }
       }

@@ -133,14 +133,6 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// 16-byte-chunk swizzle for row-major LDS tiles whose rows are a multiple of
-// 128 bytes long: chunk c of row r is stored at chunk c ^ swz16(r).  Eight
-// consecutive rows then put a given chunk in eight different bank groups
-// (16-byte MFMA operand reads), and four consecutive rows starting at a
-// multiple of 4 put a 32-byte column pair in four different bank groups
-// (transposing reads).
-__device__ __forceinline__ int swz16(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
-
 // Lazy rescaling: the running reference max only moves when a new logit
 // exceeds it by more than this (log2 units), so exp2(s - m) stays <= 2^8 and
 // the accumulator rescale (a pass over every accumulator register) is skipped

@@ -23,6 +23,15 @@
 //                                                   LDS read)
 // Each lane owns one head for the whole softmax; the LSE is over the selected
 // keys only; the sink joins the denominator in the epilogue.
+//
+// Long rows go first: the grid covers the rows twice, and a block of the first
+// half computes its row only if the row's list looks long (at least a quarter
+// of 64 evenly spaced entries valid), a block of the second half only if it
+// does not.  Both halves evaluate the same test on the same entries, so each
+// row is computed exactly once; a row of 64 tiles dispatched last would
+// otherwise keep a few CUs busy alone at the end of the launch.  Q is read
+// and the output written with non-temporal accesses: each is touched once, and
+// the gathered latent rows should keep the caches.
 #include "common.hpp"
 
 namespace attn {
@@ -57,10 +66,21 @@ void topk_mla_fwd_bf16(const Params p) {
   __shared__ int wsum[NW];
 
   const int ngroups = p.Hq / HPB;
-  const int b = blockIdx.x;
+  const int nhalf = p.T * ngroups;
+  const int second = (int)blockIdx.x >= nhalf;
+  const int b = (int)blockIdx.x - second * nhalf;
   const int i = b / ngroups;
   const int hg = b - i * ngroups;
   const int tid = threadIdx.x, lane = tid & 63;
+  {
+    int long_row = 0;
+    if (p.topk > 0) {
+      const int e = min((int)(((int64_t)lane * p.topk) >> 6), p.topk - 1);
+      const int j = p.topk_idx[(int64_t)i * p.topk_row + e];
+      long_row = __builtin_popcountll(__ballot(j >= 0 && j < p.Tk)) >= 16;
+    }
+    if (long_row == second) return;  // the other half computes this row
+  }
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   const int col = lane & 15, grp = lane >> 4;
   const int h = hg * HPB + wave * HPW + col;  // this lane's head
@@ -71,7 +91,7 @@ void topk_mla_fwd_bf16(const Params p) {
   {
     const bf16* qrow = qg + (int64_t)i * p.q_row + (int64_t)h * p.q_head + 8 * grp;
 #pragma unroll
-    for (int c = 0; c < NQC; ++c) qf[c] = *reinterpret_cast<const bf16x8*>(qrow + 32 * c);
+    for (int c = 0; c < NQC; ++c) qf[c] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(qrow + 32 * c));
   }
 
   // Tile layout in LDS, line-major: tile row r = 8 g + rr (g = 0..3) and
@@ -253,14 +273,14 @@ void topk_mla_fwd_bf16(const Params p) {
   for (int u = 0; u < HPW * DV / 8 / 64; ++u) {
     const int c = lane + 64 * u;              // 16-byte piece of the wave's tile
     const int hh = c / (DV / 8), cc = c - hh * (DV / 8);
-    *reinterpret_cast<bf16x8*>(og + (int64_t)hh * p.o_head + 8 * cc) =
-        *reinterpret_cast<const bf16x8*>(ost + hh * OS + 8 * cc);
+    __builtin_nontemporal_store(*reinterpret_cast<const bf16x8*>(ost + hh * OS + 8 * cc),
+                                reinterpret_cast<bf16x8*>(og + (int64_t)hh * p.o_head + 8 * cc));
   }
 }
 
 hipError_t launch_topk_mla_bf16(const Params& p, int sink, hipStream_t st) {
   if (p.Dqk != mla::DQK || p.Dv != mla::DV || p.Hq % mla::HPB != 0) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)((int64_t)p.T * (p.Hq / mla::HPB))), block(256);
+  const dim3 grid((unsigned)(2 * (int64_t)p.T * (p.Hq / mla::HPB))), block(256);  // two passes, see above
   if (sink == kSinkNull)
     hipLaunchKernelGGL((topk_mla_fwd_bf16<kSinkNull>), grid, block, 0, st, p);
   else
