@@ -11,6 +11,10 @@ packed as 2 x 2048, 16 heads, head dim 80, window 64, bf16, key0_bias sinks
 drawn from U(-0.1, 0.6) -- the shape of the timing paragraph of the vLLM page
 "[Bugfix][MiMo] Apply vision attention sinks in the window attention path".
 Other workloads: --workload window_16k | mla_topk | blocksparse_32k.
+--compare-unfused (window workloads) also times the page's unfused design (no-sink
+kernel + closed-form key-0 correction); --measure-merge (mla_topk) times the
+top-k lists split in two halves, each through the no-sink kernel, merged by LSE
+with the sink folded in after the merge.
 
 Prints ONE JSON line:
   value      useful TFLOP/s of the whole job = 2 (Dqk + Dv) sum |S(i,h)| / wall time
@@ -208,6 +212,102 @@ def time_gpu(case, sets_n, steps, warmup, use_graph=True):
     return wall * 1e3 / steps, kern_ms, sets[0]
 
 
+def graph_ms(step, steps, warmup):
+    """Average ms of one `step` (a zero-argument callable that enqueues its
+    launches on torch's current stream): warm up eagerly, capture `steps`
+    repetitions into one HIP graph, replay it once between HIP events."""
+    import torch
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(steps):
+            step()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record()
+    g.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) / steps
+
+
+def compare_unfused(case, steps, warmup, fused_ms):
+    """The MiMo page's unfused design on this GPU: the no-sink window kernel
+    followed by the closed-form key-0 correction of the first W + 1 rows of
+    each sequence, against the fused key0_bias kernel."""
+    import torch
+    import sink_aware_masked_amd as sam
+    d = sam.case_on_device(case, "cuda:0")
+    T, Hq = d["q"].shape[:2]
+    out = torch.empty((T, Hq, d["v"].shape[2]), dtype=d["q"].dtype, device="cuda:0")
+    lse = torch.empty((Hq, T), dtype=torch.float32, device="cuda:0")
+    nosink = dict(d, sink_mode="none", sinks=None)
+
+    def fwd_none():
+        sam.fwd(**nosink, out=out, lse=lse)
+
+    def fwd_fused():
+        sam.fwd(**d, out=out, lse=lse)
+
+    def correction():
+        sam.attn_sink_key0_correct(d["q"], d["k"], d["v"], d["cu_seqlens"], case["window"], d["sinks"],
+                                   case["scale"], out, lse)
+
+    def unfused():
+        fwd_none()
+        correction()
+    ms_fused = graph_ms(fwd_fused, steps, warmup)
+    ms_none = graph_ms(fwd_none, steps, warmup)
+    ms_unfused = graph_ms(unfused, steps, warmup)
+    ms_corr = graph_ms(correction, steps, warmup)
+    return {"fused_kernel_ms": ms_fused, "nosink_kernel_ms": ms_none, "correction_kernel_ms": ms_corr,
+            "unfused_ms": ms_unfused, "unfused_over_fused": ms_unfused / ms_fused,
+            "fused_over_nosink": ms_fused / ms_none, "fused_kernel_ms_cold": fused_ms,
+            "note": "hot cache (one input set) except fused_kernel_ms_cold; "
+                    "unfused = no-sink kernel + key-0 correction kernel"}
+
+
+def measure_merge(case, steps, warmup, fused_ms):
+    """Split-KV composition on this GPU: the top-k lists cut into two column
+    halves, each half through the no-sink kernel, then the LSE merge with the
+    null-logit sink folded in after it.  The merge alone is HBM bound: its
+    bytes are two partial (out, lse) pairs read and one written."""
+    import torch
+    import sink_aware_masked_amd as sam
+    d = sam.case_on_device(case, "cuda:0")
+    T, Hq = d["q"].shape[:2]
+    Dv = d["v"].shape[2]
+    idx = d["topk_idx"]
+    half = idx.shape[1] // 2
+    pieces = [idx[:, :half], idx[:, half:]]
+    parts = [(torch.empty((T, Hq, Dv), dtype=d["q"].dtype, device="cuda:0"),
+              torch.empty((Hq, T), dtype=torch.float32, device="cuda:0")) for _ in pieces]
+    out = torch.empty_like(parts[0][0])
+    lse = torch.empty_like(parts[0][1])
+    halves = [dict(d, sink_mode="none", sinks=None, topk_idx=pc, out=po, lse=pl)
+              for pc, (po, pl) in zip(pieces, parts)]
+
+    def merge():
+        sam.attn_sink_merge(parts, d["sinks"], case["sink_mode"], out, lse)
+
+    def split_path():  # the binding launches on torch's current stream at call time
+        for h in halves:
+            sam.fwd(**h)
+        merge()
+    for h in halves:
+        sam.fwd(**h)
+    ms_merge = graph_ms(merge, steps, warmup)
+    ms_split = graph_ms(split_path, max(1, steps // 4), max(1, warmup // 4))
+    es = out.element_size()
+    nbytes = 3 * (T * Hq * Dv * es + Hq * T * 4) + Hq * 4
+    ach = nbytes / (ms_merge * 1e-3) / 1e9
+    return {"merge_kernel_ms": ms_merge, "merge_bytes": nbytes, "merge_GBps": ach,
+            "merge_frac_hbm": ach / PEAK_HBM_GBS, "split2_fwd_plus_merge_ms": ms_split,
+            "fused_kernel_ms": fused_ms, "split_over_fused": ms_split / fused_ms}
+
+
 def cpu_baseline(case, pairs_row, dqk_dv, budget_s, out_dev, lse_dev):
     """The oracle as it stands, on a seeded row sample sized to ~budget_s."""
     import oracle
@@ -263,6 +363,10 @@ def main(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle sample budget (0: skip)")
     ap.add_argument("--compare-sink-none", action="store_true",
                     help="also time the same workload without a sink and report the ratio")
+    ap.add_argument("--compare-unfused", action="store_true",
+                    help="window workloads: also time the no-sink kernel + closed-form key-0 correction")
+    ap.add_argument("--measure-merge", action="store_true",
+                    help="top-k workload: also time the split-in-two path and the LSE merge kernel")
     ap.add_argument("--no-graph", action="store_true",
                     help="launch the timed steps one by one instead of replaying a captured graph")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -328,6 +432,19 @@ def main(argv=None):
         ms0, kern0, _ = time_gpu(base, sets_n, args.steps, args.warmup, use_graph=not args.no_graph)
         res["sink_vs_none"] = {"kernel_ms_sink": kern_ms, "kernel_ms_none": kern0,
                                "ratio": kern_ms / kern0, "ms_per_step_none": ms0}
+
+    if args.compare_unfused:
+        if kind != "window" or case["sink_mode"] != "key0_bias":
+            print("--compare-unfused needs a window workload with the key0_bias sink", file=sys.stderr)
+            return 2
+        log("[bench] unfused key-0 correction")
+        res["unfused_key0"] = compare_unfused(case, args.steps, args.warmup, kern_ms)
+    if args.measure_merge:
+        if kind != "topk":
+            print("--measure-merge needs the top-k workload", file=sys.stderr)
+            return 2
+        log("[bench] split-in-two + merge")
+        res["split_merge"] = measure_merge(case, args.steps, args.warmup, kern_ms)
 
     if args.cpu_seconds > 0:
         log(f"[bench] CPU oracle baseline (~{args.cpu_seconds:.0f} s)")

@@ -2,12 +2,18 @@
  * attn_sink.h -- C ABI of the sink-aware masked attention forward library
  * (gfx950 / MI355X).
  *
- * One entry point computes, for every packed query row i and query head h,
+ * attn_sink_fwd computes, for every packed query row i and query head h,
  *
  *     out[i, h, :] = softmax over the key set S(i, h) (plus the sink) of
  *                    scale * q[i, h, :] . k[j, h / (Hq/Hkv), :]   applied to v
  *     lse[h, i]    = natural-log log-sum-exp of those scaled logits over the
  *                    selected keys (never over the null-logit sink)
+ *
+ * Two more entry points act on such (out, lse) pairs: attn_sink_merge
+ * combines results over disjoint key sets and folds the sink in after the
+ * merge, and attn_sink_key0_correct applies the key-0 sink to a finished
+ * no-sink window result in closed form (the unfused design, kept as a
+ * comparator for the fused one).
  *
  * Sources (page titles; sections / paragraphs named):
  *   - "[Bugfix][MiMo] Apply vision attention sinks in the window attention
@@ -33,10 +39,11 @@
  *     row 16-byte aligned (bf16: multiples of 8 elements; f32: of 4).
  *   - The caller owns every buffer.  The library allocates nothing and keeps no
  *     mutable global state: calls are reentrant and may run concurrently on
- *     different streams.  Inputs are read only; out and lse are fully written
- *     (rows with an empty key set get out = 0 and lse = -inf).
- *   - Work is enqueued on `stream` as a single kernel launch; the call never
- *     synchronises and never reads device memory from the host.
+ *     different streams.  Inputs are read only.  attn_sink_fwd and
+ *     attn_sink_merge fully write out and lse (rows with an empty key set get
+ *     out = 0 and lse = -inf); attn_sink_key0_correct updates them in place.
+ *   - Each call enqueues a single kernel launch on `stream`; no call ever
+ *     synchronises or reads device memory from the host.
  *   - Errors are returned as negative attn_status codes.  Every argument error
  *     is detected on the host BEFORE anything is enqueued.  Device-side data
  *     (cu_seqlens contents, indices) is not validated -- see the
@@ -52,7 +59,7 @@
 extern "C" {
 #endif
 
-#define ATTN_SINK_ABI_VERSION 1
+#define ATTN_SINK_ABI_VERSION 2
 
 /* Which key set S(i, h) each query row attends to. */
 typedef enum attn_mask_kind {
@@ -175,6 +182,77 @@ int attn_sink_check(const attn_tensor* q, const attn_tensor* k, const attn_tenso
                     int32_t mask_kind, const attn_mask_arg* mask,
                     const float* sinks, int32_t sink_mode, float scale,
                     const attn_tensor* out, const float* lse);
+
+/*
+ * attn_sink_key0_correct -- the UNFUSED key-0 sink: a comparator for the
+ * fused ATTN_SINK_KEY0_BIAS path, after the closed-form correction paragraph of
+ * "[Bugfix][MiMo] Apply vision attention sinks in the window attention path".
+ *
+ * Takes out / lse of a WINDOW attention computed with ATTN_SINK_NONE (same
+ * q, k, v, cu_seqlens, window and scale) and rewrites in place the rows i with
+ * i - start(i) <= window, the only rows whose window holds their sequence's
+ * first key k0 = k[start(i)] (v0 likewise):
+ *     p0   = exp(scale * q[i, h, :] . k0[h / (Hq/Hkv), :] - lse[h, i])
+ *     c    = p0 * (exp(sinks[h]) - 1)
+ *     out' = (out + c * v0) / (1 + c),     lse' = lse + log1p(c)
+ * -- the ATTN_SINK_KEY0_BIAS result up to rounding.  Other rows are neither
+ * read nor written.
+ *   q, k, v, out  as for attn_sink_fwd with ATTN_MASK_WINDOW (bf16 or f32,
+ *                 T == Tk); Dqk and Dv must be whole 16-byte chunks
+ *   out, lse      device; read and overwritten (affected rows only)
+ *   sinks         device f32 [Hq], required; finite values
+ *   num_seqs, window, scale: as for attn_sink_fwd
+ * One kernel of num_seqs * (window + 1) x ceil(Hq / 4) workgroups.  Same error
+ * codes as attn_sink_fwd (ATTN_ERR_UNSUPPORTED for a head dim that is not a
+ * whole number of 16-byte chunks).
+ */
+int attn_sink_key0_correct(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
+                           const int32_t* cu_seqlens, int32_t num_seqs, int32_t window,
+                           const float* sinks, float scale, const attn_tensor* out, float* lse,
+                           hipStream_t stream);
+
+/* Host-side validation of attn_sink_key0_correct only (no device access). */
+int attn_sink_key0_correct_check(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
+                                 const int32_t* cu_seqlens, int32_t num_seqs, int32_t window,
+                                 const float* sinks, float scale, const attn_tensor* out,
+                                 const float* lse);
+
+/* Most partial results attn_sink_merge accepts in one call. */
+#define ATTN_SINK_MERGE_MAX_PARTS 8
+
+/*
+ * attn_sink_merge -- merges partial results over DISJOINT key sets of the same
+ * query rows into the result over their union, then folds in a null-logit
+ * sink once (the LSE-weighted merge the MiMo page's LSE paragraph relies on
+ * for merge_attn_states; the DeepSeek-V4 page's Implementation paragraph for
+ * folding the sink after all keys: the selected-only LSE makes this exact).
+ * With P partials (out_p, lse_p), for every row i and head h:
+ *     lse = log sum_p exp(lse_p),   out = sum_p exp(lse_p - lse) out_p
+ *     ATTN_SINK_NULL_LOGIT: out *= 1 / (1 + exp(sinks[h] - lse)); lse unchanged
+ * Partials with lse_p = -inf (empty key set) carry no weight; a row whose
+ * partials are all empty gets out = 0, lse = -inf.  The partials are meant to
+ * come from attn_sink_fwd calls with ATTN_SINK_NONE over a split key set
+ * (e.g. column ranges of a top-k list, or of a cache split across devices).
+ *   parts_out  host array of num_parts descriptors, each [T, Hq, Dv], dtype of out
+ *   parts_lse  host array of num_parts device pointers, each dense f32 [Hq, T]
+ *   num_parts  1 .. ATTN_SINK_MERGE_MAX_PARTS
+ *   sinks      device f32 [Hq]; required for ATTN_SINK_NULL_LOGIT
+ *   sink_mode  ATTN_SINK_NONE or ATTN_SINK_NULL_LOGIT (ATTN_SINK_KEY0_BIAS
+ *              returns ATTN_ERR_UNSUPPORTED: that bias belongs to the part
+ *              holding key 0)
+ *   out        [T, Hq, Dv] bf16 or f32, Dv a whole number of 16-byte chunks;
+ *   lse        device f32 [Hq, T]; both fully written, and neither may be one
+ *              of the partial buffers (ATTN_ERR_RANGE) or overlap them
+ * One kernel launch.  Errors as for attn_sink_fwd.
+ */
+int attn_sink_merge(const attn_tensor* parts_out, const float* const* parts_lse, int32_t num_parts,
+                    const float* sinks, int32_t sink_mode, const attn_tensor* out, float* lse,
+                    hipStream_t stream);
+
+/* Host-side validation of attn_sink_merge only (no device access). */
+int attn_sink_merge_check(const attn_tensor* parts_out, const float* const* parts_lse,
+                          int32_t num_parts, const float* sinks, int32_t sink_mode,
+                          const attn_tensor* out, const float* lse);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* attn_sink_strerror(int status);

@@ -29,7 +29,9 @@ DTYPE_BF16, DTYPE_F32, DTYPE_I32, DTYPE_U8 = 0, 1, 2, 3
 STATUS = {0: "ATTN_OK", -1: "ATTN_ERR_NULL", -2: "ATTN_ERR_ENUM", -3: "ATTN_ERR_SHAPE",
           -4: "ATTN_ERR_STRIDE", -5: "ATTN_ERR_HEADS", -6: "ATTN_ERR_DTYPE",
           -7: "ATTN_ERR_UNSUPPORTED", -8: "ATTN_ERR_RANGE", -9: "ATTN_ERR_LAUNCH"}
-EXPORTS = ("attn_sink_fwd", "attn_sink_check", "attn_sink_strerror", "attn_sink_abi_version")
+EXPORTS = ("attn_sink_fwd", "attn_sink_check", "attn_sink_key0_correct", "attn_sink_key0_correct_check",
+           "attn_sink_merge", "attn_sink_merge_check", "attn_sink_strerror", "attn_sink_abi_version")
+MERGE_MAX_PARTS = 8
 
 
 class AttnTensor(ctypes.Structure):
@@ -52,6 +54,16 @@ _lib.attn_sink_check.restype = ctypes.c_int
 _lib.attn_sink_check.argtypes = [_T, _T, _T, _P, ctypes.c_int32, ctypes.c_int32,
                                  ctypes.POINTER(AttnMaskArg), _P, ctypes.c_int32, ctypes.c_float,
                                  _T, _P]
+_K0 = [_T, _T, _T, _P, ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_float, _T, _P]
+_lib.attn_sink_key0_correct.restype = ctypes.c_int
+_lib.attn_sink_key0_correct.argtypes = _K0 + [_P]
+_lib.attn_sink_key0_correct_check.restype = ctypes.c_int
+_lib.attn_sink_key0_correct_check.argtypes = _K0
+_MG = [_T, ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32, _P, ctypes.c_int32, _T, _P]
+_lib.attn_sink_merge.restype = ctypes.c_int
+_lib.attn_sink_merge.argtypes = _MG + [_P]
+_lib.attn_sink_merge_check.restype = ctypes.c_int
+_lib.attn_sink_merge_check.argtypes = _MG
 _lib.attn_sink_strerror.restype = ctypes.c_char_p
 _lib.attn_sink_strerror.argtypes = [ctypes.c_int]
 _lib.attn_sink_abi_version.restype = ctypes.c_int
@@ -208,6 +220,61 @@ def fwd(q, k, v, *, mask_kind: str, scale: float, cu_seqlens=None, window=None, 
     mask = {"window": window, "topk_idx": topk_idx, "block_sel": block_sel, "block_size": block_size}
     attn_sink_fwd(q, k, v, cu_seqlens, mask_kind, mask, sinks, sink_mode, scale, out, lse, stream)
     return out, lse
+
+
+def _stream(stream, dev):
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream(dev).cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
+def attn_sink_key0_correct_check(q, k, v, cu_seqlens, num_seqs, window, sinks, scale, out, lse) -> int:
+    """Host-side validation of the unfused key-0 correction only; returns the C status."""
+    dq, dk, dv, do = (_as_desc(x) for x in (q, k, v, out))
+    return int(_lib.attn_sink_key0_correct_check(_ref(dq), _ref(dk), _ref(dv), _ptr(cu_seqlens), int(num_seqs),
+                                                 int(window), _ptr(sinks), float(scale), _ref(do), _ptr(lse)))
+
+
+def attn_sink_key0_correct(q, k, v, cu_seqlens, window, sinks, scale, out, lse, stream=None) -> None:
+    """Rewrite, in place, the out / lse of a no-sink window attention with the
+    closed-form key-0 sink (only the first window + 1 rows of each sequence).
+    Raises AttnSinkError on a non-zero status."""
+    num_seqs = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
+    dq, dk, dv, do = desc(q), desc(k), desc(v), desc(out)
+    rc = _lib.attn_sink_key0_correct(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), _ptr(cu_seqlens),
+                                     num_seqs, int(window), _ptr(sinks), float(scale), ctypes.byref(do),
+                                     _ptr(lse), ctypes.c_void_p(_stream(stream, q.device)))
+    if rc != 0:
+        raise AttnSinkError(rc)
+
+
+def _merge_args(parts, sinks, sink_mode, out, lse):
+    n = len(parts)
+    outs = (AttnTensor * max(n, 1))()
+    lses = (ctypes.c_void_p * max(n, 1))()
+    for i, (o, l) in enumerate(parts):
+        outs[i] = _as_desc(o)
+        lses[i] = _ptr(l)
+    sm = SINK_MODES[sink_mode] if isinstance(sink_mode, str) else int(sink_mode)
+    do = _as_desc(out)
+    return (outs, lses, n, _ptr(sinks), sm, _ref(do), _ptr(lse)), (outs, lses, do)
+
+
+def attn_sink_merge_check(parts, sinks, sink_mode, out, lse) -> int:
+    """Host-side validation of the merge only; parts = [(out_p, lse_p), ...]."""
+    args, keep = _merge_args(parts, sinks, sink_mode, out, lse)
+    return int(_lib.attn_sink_merge_check(*args))
+
+
+def attn_sink_merge(parts, sinks, sink_mode, out, lse, stream=None) -> None:
+    """Merge partial results over disjoint key sets, parts = [(out_p, lse_p), ...]
+    (each from a no-sink attn_sink_fwd), into out / lse, folding in a
+    null_logit sink after the merge.  Raises AttnSinkError on a non-zero status."""
+    args, keep = _merge_args(parts, sinks, sink_mode, out, lse)
+    rc = _lib.attn_sink_merge(*args, ctypes.c_void_p(_stream(stream, out.device)))
+    if rc != 0:
+        raise AttnSinkError(rc)
 
 
 def case_on_device(case: dict, device="cuda:0") -> dict:

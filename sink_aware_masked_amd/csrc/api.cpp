@@ -8,6 +8,7 @@
 
 #include "attn_sink.h"
 #include "common.hpp"
+#include "compose.hpp"
 
 #define ATTN_API extern "C" __attribute__((visibility("default")))
 
@@ -17,6 +18,8 @@ hipError_t launch_generic_f32(const Params& p, int mask, int sink, hipStream_t s
 hipError_t launch_topk_mla_bf16(const Params& p, int sink, hipStream_t st);
 hipError_t launch_blocksel_bf16(const Params& p, int sink, hipStream_t st);
 }  // namespace attn
+
+static_assert(attn::kMergeMaxParts == ATTN_SINK_MERGE_MAX_PARTS, "merge part limit");
 
 namespace {
 
@@ -206,6 +209,144 @@ ATTN_API int attn_sink_fwd(const attn_tensor* q, const attn_tensor* k, const att
     default: return ATTN_ERR_UNSUPPORTED;
   }
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+namespace {
+
+// ---------------------------------------------------------------- key-0 correction
+int prepare_key0(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
+                 const int32_t* cu_seqlens, int32_t num_seqs, int32_t window, const float* sinks,
+                 float scale, const attn_tensor* out, const float* lse, attn::Key0Params* P,
+                 bool* f32) {
+  if (!q || !k || !v || !out) return ATTN_ERR_NULL;
+  int rc;
+  if ((rc = check_tensor(q, 3)) || (rc = check_tensor(k, 3)) || (rc = check_tensor(v, 3)) ||
+      (rc = check_tensor(out, 3)))
+    return rc;
+  const int32_t dt = q->dtype;
+  if (dt != ATTN_DTYPE_BF16 && dt != ATTN_DTYPE_F32) return ATTN_ERR_DTYPE;
+  if (k->dtype != dt || v->dtype != dt || out->dtype != dt) return ATTN_ERR_DTYPE;
+  const int64_t T = q->shape[0], Hq = q->shape[1], Dqk = q->shape[2];
+  const int64_t Hkv = k->shape[1], Dv = v->shape[2];
+  if (k->shape[0] != T || v->shape[0] != T || out->shape[0] != T) return ATTN_ERR_SHAPE;
+  if (k->shape[2] != Dqk || v->shape[1] != Hkv || out->shape[1] != Hq || out->shape[2] != Dv)
+    return ATTN_ERR_SHAPE;
+  if (Hq < 1 || Hkv < 1 || Dqk < 1 || Dv < 1) return ATTN_ERR_SHAPE;
+  if (T > kMaxTokens || Hq > 4 * 65535) return ATTN_ERR_RANGE;
+  if (Hq % Hkv != 0) return ATTN_ERR_HEADS;
+  if ((rc = check_rows_aligned(q)) || (rc = check_rows_aligned(k)) || (rc = check_rows_aligned(v)) ||
+      (rc = check_rows_aligned(out)))
+    return rc;
+  const int per16 = 16 / elem_size(dt);
+  if (Dqk % per16 != 0 || Dv % per16 != 0) return ATTN_ERR_UNSUPPORTED;
+  if (!lse && T > 0) return ATTN_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(lse) % 4 != 0) return ATTN_ERR_STRIDE;
+  if (!sinks) return ATTN_ERR_NULL;
+  if (T > 0 && (!cu_seqlens || num_seqs < 1)) return cu_seqlens ? ATTN_ERR_RANGE : ATTN_ERR_NULL;
+  if (window < 0) return ATTN_ERR_RANGE;
+  if ((int64_t)num_seqs * ((int64_t)window + 1) > kMaxTokens) return ATTN_ERR_RANGE;
+  if (!(scale == scale) || scale == __builtin_huge_valf() || scale == -__builtin_huge_valf())
+    return ATTN_ERR_RANGE;
+  memset(P, 0, sizeof(*P));
+  P->q = q->data; P->k = k->data; P->v = v->data; P->out = out->data;
+  P->lse = const_cast<float*>(lse);
+  P->cu = cu_seqlens; P->sinks = sinks;
+  P->q_row = q->stride[0]; P->q_head = q->stride[1];
+  P->k_row = k->stride[0]; P->k_head = k->stride[1];
+  P->v_row = v->stride[0]; P->v_head = v->stride[1];
+  P->o_row = out->stride[0]; P->o_head = out->stride[1];
+  P->T = (int)T; P->Hq = (int)Hq; P->group = (int)(Hq / Hkv); P->Dqk = (int)Dqk; P->Dv = (int)Dv;
+  P->num_seqs = num_seqs; P->window = window; P->scale = scale;
+  *f32 = dt == ATTN_DTYPE_F32;
+  return ATTN_OK;
+}
+
+// ---------------------------------------------------------------- merge
+int prepare_merge(const attn_tensor* parts_out, const float* const* parts_lse, int32_t num_parts,
+                  const float* sinks, int32_t sink_mode, const attn_tensor* out, const float* lse,
+                  attn::MergeParams* P, bool* f32) {
+  if (!parts_out || !parts_lse || !out) return ATTN_ERR_NULL;
+  if (num_parts < 1 || num_parts > attn::kMergeMaxParts) return ATTN_ERR_RANGE;
+  if (sink_mode < ATTN_SINK_NONE || sink_mode > ATTN_SINK_NULL_LOGIT) return ATTN_ERR_ENUM;
+  if (sink_mode == ATTN_SINK_KEY0_BIAS) return ATTN_ERR_UNSUPPORTED;
+  if (sink_mode == ATTN_SINK_NULL_LOGIT && !sinks) return ATTN_ERR_NULL;
+  int rc;
+  if ((rc = check_tensor(out, 3))) return rc;
+  const int32_t dt = out->dtype;
+  if (dt != ATTN_DTYPE_BF16 && dt != ATTN_DTYPE_F32) return ATTN_ERR_DTYPE;
+  const int64_t T = out->shape[0], Hq = out->shape[1], Dv = out->shape[2];
+  if (Hq < 1 || Dv < 1) return ATTN_ERR_SHAPE;
+  if (T > kMaxTokens || Hq > 65535) return ATTN_ERR_RANGE;
+  if ((rc = check_rows_aligned(out))) return rc;
+  if (Dv % (16 / elem_size(dt)) != 0) return ATTN_ERR_UNSUPPORTED;
+  if (!lse && T > 0) return ATTN_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(lse) % 4 != 0) return ATTN_ERR_STRIDE;
+  memset(P, 0, sizeof(*P));
+  for (int p = 0; p < num_parts; ++p) {
+    const attn_tensor* t = parts_out + p;
+    if ((rc = check_tensor(t, 3))) return rc;
+    if (t->dtype != dt) return ATTN_ERR_DTYPE;
+    if (t->shape[0] != T || t->shape[1] != Hq || t->shape[2] != Dv) return ATTN_ERR_SHAPE;
+    if ((rc = check_rows_aligned(t))) return rc;
+    if (!parts_lse[p] && T > 0) return ATTN_ERR_NULL;
+    if (reinterpret_cast<uintptr_t>(parts_lse[p]) % 4 != 0) return ATTN_ERR_STRIDE;
+    if (T > 0 && (t->data == out->data || parts_lse[p] == lse)) return ATTN_ERR_RANGE;  // no in-place merge
+    P->part_out[p] = t->data;
+    P->part_lse[p] = parts_lse[p];
+    P->p_row[p] = t->stride[0];
+    P->p_head[p] = t->stride[1];
+  }
+  P->out = out->data;
+  P->lse = const_cast<float*>(lse);
+  P->sinks = sinks;
+  P->o_row = out->stride[0]; P->o_head = out->stride[1];
+  P->T = (int)T; P->Hq = (int)Hq; P->Dv = (int)Dv; P->nparts = num_parts;
+  P->nchunks = T * Hq * (Dv / (16 / elem_size(dt)));
+  *f32 = dt == ATTN_DTYPE_F32;
+  return ATTN_OK;
+}
+
+}  // namespace
+
+ATTN_API int attn_sink_key0_correct_check(const attn_tensor* q, const attn_tensor* k,
+                                          const attn_tensor* v, const int32_t* cu_seqlens,
+                                          int32_t num_seqs, int32_t window, const float* sinks,
+                                          float scale, const attn_tensor* out, const float* lse) {
+  attn::Key0Params P;
+  bool f32;
+  return prepare_key0(q, k, v, cu_seqlens, num_seqs, window, sinks, scale, out, lse, &P, &f32);
+}
+
+ATTN_API int attn_sink_key0_correct(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
+                                    const int32_t* cu_seqlens, int32_t num_seqs, int32_t window,
+                                    const float* sinks, float scale, const attn_tensor* out, float* lse,
+                                    hipStream_t stream) {
+  attn::Key0Params P;
+  bool f32;
+  const int rc = prepare_key0(q, k, v, cu_seqlens, num_seqs, window, sinks, scale, out, lse, &P, &f32);
+  if (rc != ATTN_OK) return rc;
+  if (P.T == 0) return ATTN_OK;
+  return attn::launch_key0_correct(P, f32, stream) == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+ATTN_API int attn_sink_merge_check(const attn_tensor* parts_out, const float* const* parts_lse,
+                                   int32_t num_parts, const float* sinks, int32_t sink_mode,
+                                   const attn_tensor* out, const float* lse) {
+  attn::MergeParams P;
+  bool f32;
+  return prepare_merge(parts_out, parts_lse, num_parts, sinks, sink_mode, out, lse, &P, &f32);
+}
+
+ATTN_API int attn_sink_merge(const attn_tensor* parts_out, const float* const* parts_lse,
+                             int32_t num_parts, const float* sinks, int32_t sink_mode,
+                             const attn_tensor* out, float* lse, hipStream_t stream) {
+  attn::MergeParams P;
+  bool f32;
+  const int rc = prepare_merge(parts_out, parts_lse, num_parts, sinks, sink_mode, out, lse, &P, &f32);
+  if (rc != ATTN_OK) return rc;
+  if (P.T == 0) return ATTN_OK;
+  return attn::launch_merge(P, f32, sink_mode == ATTN_SINK_NULL_LOGIT, stream) == hipSuccess
+             ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
 ATTN_API const char* attn_sink_strerror(int status) {

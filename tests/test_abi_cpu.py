@@ -168,3 +168,78 @@ def test_binding_fails_loudly_without_library(tmp_path):
     code = "import sink_aware_masked_amd"
     r = subprocess.run([sys.executable, "-c", code], cwd=tmp_path, capture_output=True, text=True)
     assert r.returncode != 0 and "not built" in r.stderr
+
+
+# --------------------------------------------- unfused key-0 correction / merge
+def key0_args(T=256, Hq=16, Hkv=4, D=80, dtype=torch.bfloat16, W=64):
+    a = window_args(T=T, Hq=Hq, Hkv=Hkv, D=D, dtype=dtype, W=W)
+    return dict(q=a["q"], k=a["k"], v=a["v"], cu_seqlens=a["cu_seqlens"], num_seqs=2, window=W,
+                sinks=torch.zeros(Hq), scale=0.1, out=a["out"], lse=a["lse"])
+
+
+def key0_check(sam, a):
+    return sam.attn_sink_key0_correct_check(a["q"], a["k"], a["v"], a["cu_seqlens"], a["num_seqs"], a["window"],
+                                            a["sinks"], a["scale"], a["out"], a["lse"])
+
+
+def test_key0_correct_validation(sam):
+    for D in (64, 80, 128):
+        assert key0_check(sam, key0_args(D=D)) == 0
+    assert key0_check(sam, key0_args(D=48, dtype=torch.float32)) == 0
+    a = key0_args()
+    for over, expect in (({"sinks": None}, "ATTN_ERR_NULL"), ({"cu_seqlens": None}, "ATTN_ERR_NULL"),
+                         ({"lse": None}, "ATTN_ERR_NULL"), ({"window": -1}, "ATTN_ERR_RANGE"),
+                         ({"scale": float("inf")}, "ATTN_ERR_RANGE"),
+                         ({"out": torch.empty(256, 16, 80, dtype=torch.float32)}, "ATTN_ERR_DTYPE"),
+                         ({"k": torch.empty(255, 4, 80, dtype=torch.bfloat16)}, "ATTN_ERR_SHAPE"),
+                         ({"k": torch.empty(256, 3, 80, dtype=torch.bfloat16),
+                           "v": torch.empty(256, 3, 80, dtype=torch.bfloat16)}, "ATTN_ERR_HEADS"),
+                         ({"q": torch.empty(256, 16, 84, dtype=torch.bfloat16)[:, :, :80]}, "ATTN_ERR_STRIDE")):
+        b = dict(a)
+        b.update(over)
+        assert sam.STATUS[key0_check(sam, b)] == expect, (over.keys(), expect)
+    # an f32 head dim of 6 is not a whole number of 16-byte chunks
+    f = key0_args(D=4, dtype=torch.float32)
+    for k_, h in (("q", 16), ("k", 4), ("v", 4), ("out", 16)):
+        f[k_] = torch.empty(256, h, 8, dtype=torch.float32)[:, :, :6]
+    assert sam.STATUS[key0_check(sam, f)] in ("ATTN_ERR_UNSUPPORTED", "ATTN_ERR_STRIDE")
+
+
+def merge_args(P=2, T=64, Hq=8, Dv=128, dtype=torch.bfloat16):
+    parts = [(torch.empty(T, Hq, Dv, dtype=dtype), torch.empty(Hq, T)) for _ in range(P)]
+    return dict(parts=parts, sinks=torch.zeros(Hq), sink_mode="null_logit",
+                out=torch.empty(T, Hq, Dv, dtype=dtype), lse=torch.empty(Hq, T))
+
+
+def merge_check(sam, a):
+    return sam.attn_sink_merge_check(a["parts"], a["sinks"], a["sink_mode"], a["out"], a["lse"])
+
+
+def test_merge_validation(sam):
+    for P in (1, 2, sam.MERGE_MAX_PARTS):
+        assert merge_check(sam, merge_args(P=P)) == 0
+    assert merge_check(sam, merge_args(dtype=torch.float32, Dv=4)) == 0
+    a = merge_args()
+    a["sink_mode"], a["sinks"] = "none", None
+    assert merge_check(sam, a) == 0
+
+    def bad(expect, **over):
+        b = merge_args()
+        b.update(over)
+        assert sam.STATUS[merge_check(sam, b)] == expect, (over.keys(), expect)
+
+    bad("ATTN_ERR_RANGE", parts=[])
+    bad("ATTN_ERR_RANGE", parts=merge_args(P=sam.MERGE_MAX_PARTS + 1)["parts"])
+    bad("ATTN_ERR_UNSUPPORTED", sink_mode="key0_bias")
+    bad("ATTN_ERR_ENUM", sink_mode=3)
+    bad("ATTN_ERR_NULL", sinks=None)
+    bad("ATTN_ERR_NULL", lse=None)
+    bad("ATTN_ERR_DTYPE", out=torch.empty(64, 8, 128, dtype=torch.float32))
+    bad("ATTN_ERR_SHAPE", parts=[(torch.empty(64, 8, 64, dtype=torch.bfloat16), torch.empty(8, 64))] * 2)
+    bad("ATTN_ERR_NULL", parts=[(torch.empty(64, 8, 128, dtype=torch.bfloat16), None)] * 2)
+    b = merge_args()
+    b["out"] = b["parts"][1][0]  # writing into a partial is refused
+    assert sam.STATUS[merge_check(sam, b)] == "ATTN_ERR_RANGE"
+    b = merge_args()
+    b["lse"] = b["parts"][0][1]
+    assert sam.STATUS[merge_check(sam, b)] == "ATTN_ERR_RANGE"
