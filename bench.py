@@ -14,7 +14,8 @@ Other workloads: --workload window_16k | mla_topk | blocksparse_32k.
 --compare-unfused (window workloads) also times the page's unfused design (no-sink
 kernel + closed-form key-0 correction); --measure-merge (mla_topk) times the
 top-k lists split in two halves, each through the no-sink kernel, merged by LSE
-with the sink folded in after the merge.
+with the sink folded in after the merge; --measure-cp (blocksparse_32k) times the
+context-parallel reorder of K/V from an 8-rank load-balanced layout.
 
 Prints ONE JSON line:
   value      useful TFLOP/s of the whole job = 2 (Dqk + Dv) sum |S(i,h)| / wall time
@@ -308,6 +309,41 @@ def measure_merge(case, steps, warmup, fused_ms):
             "fused_kernel_ms": fused_ms, "split_over_fused": ms_split / fused_ms}
 
 
+def measure_cp(case, steps, warmup, cp_size=8):
+    """Context-parallel reorder on this GPU: K and V of the workload as an
+    all-gather of cp_size load-balanced shards would hold them, put into global
+    token order (two row scatters), and the document segments derived from the
+    reordered position ids.  The scatters are HBM bound: each row is read once
+    and written once, plus the int64 index."""
+    import torch
+    import sink_aware_masked_amd as sam
+    d = sam.case_on_device(case, "cuda:0")
+    T = d["q"].shape[0]
+    slots = torch.empty(T, dtype=torch.int64, device="cuda:0")
+    sam.attn_sink_cp_slots(cp_size, T // cp_size, -1, slots)
+    lens = np.diff(case["cu_seqlens"])
+    pos = torch.from_numpy(np.concatenate([np.arange(n) for n in lens]).astype(np.int64)).to("cuda:0")
+    gathered = [d["k"][slots], d["v"][slots]]
+    glob = [torch.empty_like(x) for x in gathered]
+    pos_g, pos_glob = pos[slots], torch.empty_like(pos)
+    cu = torch.empty(len(case["cu_seqlens"]), dtype=torch.int32, device="cuda:0")
+    nd = torch.empty(1, dtype=torch.int32, device="cuda:0")
+
+    def reorder():
+        for src, dst in zip(gathered, glob):
+            sam.attn_sink_cp_permute_rows(src, slots, True, dst)
+
+    def documents():
+        sam.attn_sink_cp_permute_rows(pos_g, slots, True, pos_glob)
+        sam.attn_sink_cp_documents(pos_glob, None, cu, nd)
+    ms_kv = graph_ms(reorder, steps, warmup)
+    ms_doc = graph_ms(documents, steps, warmup)
+    nbytes = sum(2 * x.numel() * x.element_size() for x in gathered) + 2 * slots.numel() * 8
+    ach = nbytes / (ms_kv * 1e-3) / 1e9
+    return {"cp_size": cp_size, "kv_reorder_ms": ms_kv, "kv_reorder_bytes": nbytes, "kv_reorder_GBps": ach,
+            "kv_reorder_frac_hbm": ach / PEAK_HBM_GBS, "positions_reorder_and_documents_ms": ms_doc}
+
+
 def cpu_baseline(case, pairs_row, dqk_dv, budget_s, out_dev, lse_dev):
     """The oracle as it stands, on a seeded row sample sized to ~budget_s."""
     import oracle
@@ -367,6 +403,8 @@ def main(argv=None):
                     help="window workloads: also time the no-sink kernel + closed-form key-0 correction")
     ap.add_argument("--measure-merge", action="store_true",
                     help="top-k workload: also time the split-in-two path and the LSE merge kernel")
+    ap.add_argument("--measure-cp", action="store_true",
+                    help="block-sparse workload: also time the context-parallel K/V reorder and document derivation")
     ap.add_argument("--no-graph", action="store_true",
                     help="launch the timed steps one by one instead of replaying a captured graph")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -445,6 +483,13 @@ def main(argv=None):
             return 2
         log("[bench] split-in-two + merge")
         res["split_merge"] = measure_merge(case, args.steps, args.warmup, kern_ms)
+
+    if args.measure_cp:
+        if kind != "blocksel":
+            print("--measure-cp needs the block-sparse workload", file=sys.stderr)
+            return 2
+        log("[bench] context-parallel reorder")
+        res["cp_reorder"] = measure_cp(case, args.steps, args.warmup)
 
     if args.cpu_seconds > 0:
         log(f"[bench] CPU oracle baseline (~{args.cpu_seconds:.0f} s)")

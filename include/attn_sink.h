@@ -13,7 +13,9 @@
  * combines results over disjoint key sets and folds the sink in after the
  * merge, and attn_sink_key0_correct applies the key-0 sink to a finished
  * no-sink window result in closed form (the unfused design, kept as a
- * comparator for the fused one).
+ * comparator for the fused one).  The attn_sink_cp_* calls are the
+ * context-parallel reorder primitives that bring sharded K/V into global token
+ * order and derive the document segments.
  *
  * Sources (page titles; sections / paragraphs named):
  *   - "[Bugfix][MiMo] Apply vision attention sinks in the window attention
@@ -95,7 +97,8 @@ typedef enum attn_dtype {
   ATTN_DTYPE_BF16 = 0,
   ATTN_DTYPE_F32 = 1,
   ATTN_DTYPE_I32 = 2,
-  ATTN_DTYPE_U8 = 3
+  ATTN_DTYPE_U8 = 3,
+  ATTN_DTYPE_I64 = 4   /* position ids / slot indices (context-parallel reorder) */
 } attn_dtype;
 
 typedef enum attn_status {
@@ -253,6 +256,69 @@ int attn_sink_merge(const attn_tensor* parts_out, const float* const* parts_lse,
 int attn_sink_merge_check(const attn_tensor* parts_out, const float* const* parts_lse,
                           int32_t num_parts, const float* sinks, int32_t sink_mode,
                           const attn_tensor* out, const float* lse);
+
+/*
+ * Context-parallel reorder primitives (NeMo AutoModel "cp_sparse_attn" API
+ * page: cp_load_balanced_global_slots, order_by_positions /
+ * restore_by_positions, cp_document_ids).  Under causal context parallelism a
+ * rank holds a non-contiguous, load-balanced part of the sequence; before a
+ * block-sparse layer can attend over the global sequence, K/V gathered from
+ * every rank are put into global token order, and the packed position ids
+ * give the documents.  Each call is one kernel launch on `stream`; integer and
+ * byte results are exact.
+ *
+ * attn_sink_cp_slots -- global slot index of every local slot: the sequence of
+ * T = cp_size * t_local tokens is cut into 2 * cp_size chunks of t_local / 2,
+ * and rank r holds chunks r and 2 * cp_size - 1 - r, in that order.
+ *   rank   0 .. cp_size - 1: writes t_local slots of that rank;
+ *          -1: writes cp_size * t_local slots, rank-major (the order of an
+ *          all-gather of the shards)
+ *   slots  device int64, that many entries
+ * ATTN_ERR_RANGE if cp_size < 1, t_local is odd or negative, or rank is out
+ * of range.
+ */
+int attn_sink_cp_slots(int32_t cp_size, int64_t t_local, int32_t rank, int64_t* slots, hipStream_t stream);
+int attn_sink_cp_slots_check(int32_t cp_size, int64_t t_local, int32_t rank, const int64_t* slots);
+
+/*
+ * attn_sink_cp_permute_rows -- moves whole rows (everything past dim 0) of a
+ * rank 1..4 tensor:
+ *   scatter == 1: dst[index[i]] = src[i]   (order_by_positions: gathered rows,
+ *                 index = their global positions -> global token order)
+ *   scatter == 0: dst[i] = src[index[i]]   (restore_by_positions: global-ordered
+ *                 rows -> the rows at the given positions, in that order)
+ * for i < n; src (scatter) or dst (gather) has n rows.  index: device int64
+ * [n].  With scatter, an index outside [0, dst rows) drops that row; with
+ * gather, an index outside [0, src rows) writes a zero row.  For a permutation
+ * the two are inverse to each other.  Rows must be dense; rows move in 16-,
+ * 8- or 4-byte chunks, the widest dividing the row length, the row strides and
+ * the base addresses (none: ATTN_ERR_UNSUPPORTED).  src and dst share dtype
+ * and row shape and must not overlap (the same buffer gives ATTN_ERR_RANGE).
+ * Duplicate scatter targets are a caller error (one of the rows wins).
+ */
+int attn_sink_cp_permute_rows(const attn_tensor* src, const int64_t* index, int64_t n, int32_t scatter,
+                              const attn_tensor* dst, hipStream_t stream);
+int attn_sink_cp_permute_rows_check(const attn_tensor* src, const int64_t* index, int64_t n, int32_t scatter,
+                                    const attn_tensor* dst);
+
+/*
+ * attn_sink_cp_documents -- from global-ordered position ids (device int64
+ * [T]) of packed documents:
+ *   doc_ids     device int32 [T] or NULL: cumsum(positions == 0) - 1 (the
+ *               page's cp_document_ids; -1 before the first position-0 token)
+ *   cu_seqlens  device int32 [max_docs + 1] or NULL: segment boundaries for
+ *               attn_sink_fwd -- 0, every later index whose position is 0,
+ *               then T (token 0 always opens a segment, so with positions[0]
+ *               == 0 the segments are exactly the documents)
+ *   num_docs    device int32 scalar or NULL: number of segments.  If it
+ *               exceeds max_docs only the first max_docs boundaries are
+ *               written and T is not.
+ * One workgroup scans the positions (one pass, 16384 per step).
+ */
+int attn_sink_cp_documents(const int64_t* positions, int64_t T, int32_t* doc_ids, int32_t* cu_seqlens,
+                           int32_t max_docs, int32_t* num_docs, hipStream_t stream);
+int attn_sink_cp_documents_check(const int64_t* positions, int64_t T, const int32_t* doc_ids,
+                                 const int32_t* cu_seqlens, int32_t max_docs, const int32_t* num_docs);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* attn_sink_strerror(int status);

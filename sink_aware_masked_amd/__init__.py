@@ -25,12 +25,14 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 MASK_KINDS = {"window": 0, "topk": 1, "blocksel": 2}
 SINK_MODES = {"none": 0, "key0_bias": 1, "null_logit": 2}
-DTYPE_BF16, DTYPE_F32, DTYPE_I32, DTYPE_U8 = 0, 1, 2, 3
+DTYPE_BF16, DTYPE_F32, DTYPE_I32, DTYPE_U8, DTYPE_I64 = 0, 1, 2, 3, 4
 STATUS = {0: "ATTN_OK", -1: "ATTN_ERR_NULL", -2: "ATTN_ERR_ENUM", -3: "ATTN_ERR_SHAPE",
           -4: "ATTN_ERR_STRIDE", -5: "ATTN_ERR_HEADS", -6: "ATTN_ERR_DTYPE",
           -7: "ATTN_ERR_UNSUPPORTED", -8: "ATTN_ERR_RANGE", -9: "ATTN_ERR_LAUNCH"}
 EXPORTS = ("attn_sink_fwd", "attn_sink_check", "attn_sink_key0_correct", "attn_sink_key0_correct_check",
-           "attn_sink_merge", "attn_sink_merge_check", "attn_sink_strerror", "attn_sink_abi_version")
+           "attn_sink_merge", "attn_sink_merge_check", "attn_sink_cp_slots", "attn_sink_cp_slots_check",
+           "attn_sink_cp_permute_rows", "attn_sink_cp_permute_rows_check", "attn_sink_cp_documents",
+           "attn_sink_cp_documents_check", "attn_sink_strerror", "attn_sink_abi_version")
 MERGE_MAX_PARTS = 8
 
 
@@ -64,6 +66,19 @@ _lib.attn_sink_merge.restype = ctypes.c_int
 _lib.attn_sink_merge.argtypes = _MG + [_P]
 _lib.attn_sink_merge_check.restype = ctypes.c_int
 _lib.attn_sink_merge_check.argtypes = _MG
+_I64, _I32 = ctypes.c_int64, ctypes.c_int32
+_lib.attn_sink_cp_slots.restype = ctypes.c_int
+_lib.attn_sink_cp_slots.argtypes = [_I32, _I64, _I32, _P, _P]
+_lib.attn_sink_cp_slots_check.restype = ctypes.c_int
+_lib.attn_sink_cp_slots_check.argtypes = [_I32, _I64, _I32, _P]
+_lib.attn_sink_cp_permute_rows.restype = ctypes.c_int
+_lib.attn_sink_cp_permute_rows.argtypes = [_T, _P, _I64, _I32, _T, _P]
+_lib.attn_sink_cp_permute_rows_check.restype = ctypes.c_int
+_lib.attn_sink_cp_permute_rows_check.argtypes = [_T, _P, _I64, _I32, _T]
+_lib.attn_sink_cp_documents.restype = ctypes.c_int
+_lib.attn_sink_cp_documents.argtypes = [_P, _I64, _P, _P, _I32, _P, _P]
+_lib.attn_sink_cp_documents_check.restype = ctypes.c_int
+_lib.attn_sink_cp_documents_check.argtypes = [_P, _I64, _P, _P, _I32, _P]
 _lib.attn_sink_strerror.restype = ctypes.c_char_p
 _lib.attn_sink_strerror.argtypes = [ctypes.c_int]
 _lib.attn_sink_abi_version.restype = ctypes.c_int
@@ -87,7 +102,7 @@ def attn_sink_abi_version() -> int:
 def _dtype_code(t) -> int:
     import torch
     codes = {torch.bfloat16: DTYPE_BF16, torch.float32: DTYPE_F32, torch.int32: DTYPE_I32,
-             torch.uint8: DTYPE_U8, torch.bool: DTYPE_U8}
+             torch.uint8: DTYPE_U8, torch.bool: DTYPE_U8, torch.int64: DTYPE_I64}
     if t.dtype not in codes:
         raise TypeError(f"unsupported tensor dtype {t.dtype}")
     return codes[t.dtype]
@@ -275,6 +290,49 @@ def attn_sink_merge(parts, sinks, sink_mode, out, lse, stream=None) -> None:
     rc = _lib.attn_sink_merge(*args, ctypes.c_void_p(_stream(stream, out.device)))
     if rc != 0:
         raise AttnSinkError(rc)
+
+
+def _check_rc(rc):
+    if rc != 0:
+        raise AttnSinkError(rc)
+
+
+def attn_sink_cp_slots_check(cp_size, t_local, rank, slots) -> int:
+    return int(_lib.attn_sink_cp_slots_check(int(cp_size), int(t_local), int(rank), _ptr(slots)))
+
+
+def attn_sink_cp_slots(cp_size, t_local, rank, slots, stream=None) -> None:
+    """Global slot of every local slot under load-balanced causal CP (rank -1:
+    all ranks, rank-major) into the int64 device tensor `slots`."""
+    _check_rc(_lib.attn_sink_cp_slots(int(cp_size), int(t_local), int(rank), _ptr(slots),
+                                      ctypes.c_void_p(_stream(stream, slots.device))))
+
+
+def attn_sink_cp_permute_rows_check(src, index, n, scatter, dst) -> int:
+    ds, dd = _as_desc(src), _as_desc(dst)
+    return int(_lib.attn_sink_cp_permute_rows_check(_ref(ds), _ptr(index), int(n), int(scatter), _ref(dd)))
+
+
+def attn_sink_cp_permute_rows(src, index, scatter, dst, stream=None) -> None:
+    """scatter: dst[index[i]] = src[i] (order_by_positions); gather:
+    dst[i] = src[index[i]] (restore_by_positions).  index: int64 device tensor."""
+    ds, dd = desc(src), desc(dst)
+    _check_rc(_lib.attn_sink_cp_permute_rows(ctypes.byref(ds), _ptr(index), int(index.numel()), int(bool(scatter)),
+                                             ctypes.byref(dd), ctypes.c_void_p(_stream(stream, src.device))))
+
+
+def attn_sink_cp_documents_check(positions, T, doc_ids, cu_seqlens, max_docs, num_docs) -> int:
+    return int(_lib.attn_sink_cp_documents_check(_ptr(positions), int(T), _ptr(doc_ids), _ptr(cu_seqlens),
+                                                 int(max_docs), _ptr(num_docs)))
+
+
+def attn_sink_cp_documents(positions, doc_ids=None, cu_seqlens=None, num_docs=None, stream=None) -> None:
+    """Document ids (cumsum(positions == 0) - 1) and segment boundaries of
+    global-ordered int64 position ids; cu_seqlens holds max_docs + 1 entries."""
+    max_docs = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
+    _check_rc(_lib.attn_sink_cp_documents(_ptr(positions), int(positions.numel()), _ptr(doc_ids),
+                                          _ptr(cu_seqlens), int(max_docs), _ptr(num_docs),
+                                          ctypes.c_void_p(_stream(stream, positions.device))))
 
 
 def case_on_device(case: dict, device="cuda:0") -> dict:

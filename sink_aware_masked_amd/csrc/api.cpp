@@ -9,6 +9,7 @@
 #include "attn_sink.h"
 #include "common.hpp"
 #include "compose.hpp"
+#include "cp.hpp"
 
 #define ATTN_API extern "C" __attribute__((visibility("default")))
 
@@ -35,11 +36,12 @@ int elem_size(int32_t dt) {
     case ATTN_DTYPE_F32: return 4;
     case ATTN_DTYPE_I32: return 4;
     case ATTN_DTYPE_U8: return 1;
+    case ATTN_DTYPE_I64: return 8;
     default: return 0;
   }
 }
 
-bool valid_dtype(int32_t dt) { return dt >= ATTN_DTYPE_BF16 && dt <= ATTN_DTYPE_U8; }
+bool valid_dtype(int32_t dt) { return dt >= ATTN_DTYPE_BF16 && dt <= ATTN_DTYPE_I64; }
 
 // Rank, non-negative sizes / strides, unit inner stride.
 // A NULL data pointer is accepted only for an empty tensor.
@@ -347,6 +349,147 @@ ATTN_API int attn_sink_merge(const attn_tensor* parts_out, const float* const* p
   if (P.T == 0) return ATTN_OK;
   return attn::launch_merge(P, f32, sink_mode == ATTN_SINK_NULL_LOGIT, stream) == hipSuccess
              ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+namespace {
+
+// ---------------------------------------------------------------- context-parallel reorder
+int prepare_cp_slots(int32_t cp_size, int64_t t_local, int32_t rank, const int64_t* slots,
+                     attn::CpSlotsParams* P) {
+  if (cp_size < 1 || t_local < 0 || t_local % 2 != 0 || t_local > ((int64_t)1 << 40)) return ATTN_ERR_RANGE;
+  if (rank < -1 || rank >= cp_size) return ATTN_ERR_RANGE;
+  const int64_t n = rank < 0 ? (int64_t)cp_size * t_local : t_local;
+  if (n > 0 && !slots) return ATTN_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(slots) % 8 != 0) return ATTN_ERR_STRIDE;
+  P->slots = const_cast<int64_t*>(slots);
+  P->t_local = t_local;
+  P->n = n;
+  P->cp_size = cp_size;
+  P->rank = rank;
+  return ATTN_OK;
+}
+
+// Rank 1..4 tensors whose rows (everything past dim 0) are dense.
+int check_rows_tensor(const attn_tensor* t, int64_t* row_bytes) {
+  if (!t) return ATTN_ERR_NULL;
+  if (!valid_dtype(t->dtype)) return ATTN_ERR_ENUM;
+  if (t->ndim < 1 || t->ndim > 4) return ATTN_ERR_SHAPE;
+  int64_t dense = 1;
+  bool empty = false;
+  for (int d = t->ndim - 1; d >= 0; --d) {
+    if (t->shape[d] < 0) return ATTN_ERR_SHAPE;
+    if (t->stride[d] < 0) return ATTN_ERR_STRIDE;
+    empty = empty || t->shape[d] == 0;
+    if (d > 0) {
+      if (t->stride[d] != dense && t->shape[d] > 1) return ATTN_ERR_STRIDE;
+      dense *= t->shape[d];
+    }
+  }
+  if (!t->data && !empty) return ATTN_ERR_NULL;
+  *row_bytes = dense * elem_size(t->dtype);
+  if (t->shape[0] > 1 && t->stride[0] < dense) return ATTN_ERR_STRIDE;
+  return ATTN_OK;
+}
+
+// Widest chunk (16, 8 or 4 bytes) dividing the row length, both row strides
+// and both base addresses; 0 if not even 4 does.
+int chunk_width(int64_t row_bytes, const attn_tensor* a, const attn_tensor* b) {
+  const uint64_t bits = (uint64_t)row_bytes | (uint64_t)(a->stride[0] * elem_size(a->dtype)) |
+                        (uint64_t)(b->stride[0] * elem_size(b->dtype)) |
+                        (uint64_t)reinterpret_cast<uintptr_t>(a->data) | (uint64_t)reinterpret_cast<uintptr_t>(b->data);
+  return bits % 16 == 0 ? 16 : bits % 8 == 0 ? 8 : bits % 4 == 0 ? 4 : 0;
+}
+
+int prepare_permute(const attn_tensor* src, const int64_t* index, int64_t n, int32_t scatter,
+                    const attn_tensor* dst, attn::PermuteParams* P) {
+  if (!src || !dst) return ATTN_ERR_NULL;
+  if (scatter != 0 && scatter != 1) return ATTN_ERR_ENUM;
+  int64_t rs, rd;
+  int rc;
+  if ((rc = check_rows_tensor(src, &rs)) || (rc = check_rows_tensor(dst, &rd))) return rc;
+  if (src->dtype != dst->dtype) return ATTN_ERR_DTYPE;
+  if (src->ndim != dst->ndim) return ATTN_ERR_SHAPE;
+  for (int d = 1; d < src->ndim; ++d)
+    if (src->shape[d] != dst->shape[d]) return ATTN_ERR_SHAPE;
+  if (n < 0 || (scatter ? src->shape[0] : dst->shape[0]) != n) return ATTN_ERR_SHAPE;
+  const int cw = chunk_width(rs, src, dst);
+  if (cw == 0 || rs / cw > 0x7fffffff) return ATTN_ERR_UNSUPPORTED;
+  if (n > 0 && !index) return ATTN_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(index) % 8 != 0) return ATTN_ERR_STRIDE;
+  if (n > 0 && rs > 0 && src->data == dst->data) return ATTN_ERR_RANGE;  // not in place
+  const int es = elem_size(src->dtype);
+  P->src = static_cast<const char*>(src->data);
+  P->dst = static_cast<char*>(dst->data);
+  P->index = index;
+  P->src_row = src->stride[0] * es;
+  P->dst_row = dst->stride[0] * es;
+  P->src_rows = src->shape[0];
+  P->dst_rows = dst->shape[0];
+  P->n = n;
+  P->chunks = (int)(rs / cw);
+  P->chunk_bytes = cw;
+  P->scatter = scatter;
+  return ATTN_OK;
+}
+
+int prepare_cp_documents(const int64_t* positions, int64_t T, const int32_t* doc_ids, const int32_t* cu_seqlens,
+                         int32_t max_docs, const int32_t* num_docs, attn::CpDocParams* P) {
+  if (T < 0 || T > kMaxTokens || max_docs < 0) return ATTN_ERR_RANGE;
+  if (T > 0 && !positions) return ATTN_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(positions) % 8 != 0 || reinterpret_cast<uintptr_t>(doc_ids) % 4 != 0 ||
+      reinterpret_cast<uintptr_t>(cu_seqlens) % 4 != 0 || reinterpret_cast<uintptr_t>(num_docs) % 4 != 0)
+    return ATTN_ERR_STRIDE;
+  P->positions = positions;
+  P->T = T;
+  P->doc_ids = const_cast<int32_t*>(doc_ids);
+  P->cu = const_cast<int32_t*>(cu_seqlens);
+  P->num_docs = const_cast<int32_t*>(num_docs);
+  P->max_docs = max_docs;
+  return ATTN_OK;
+}
+
+}  // namespace
+
+ATTN_API int attn_sink_cp_slots_check(int32_t cp_size, int64_t t_local, int32_t rank, const int64_t* slots) {
+  attn::CpSlotsParams P;
+  return prepare_cp_slots(cp_size, t_local, rank, slots, &P);
+}
+
+ATTN_API int attn_sink_cp_slots(int32_t cp_size, int64_t t_local, int32_t rank, int64_t* slots,
+                                hipStream_t stream) {
+  attn::CpSlotsParams P;
+  const int rc = prepare_cp_slots(cp_size, t_local, rank, slots, &P);
+  if (rc != ATTN_OK || P.n == 0) return rc;
+  return attn::launch_cp_slots(P, stream) == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+ATTN_API int attn_sink_cp_permute_rows_check(const attn_tensor* src, const int64_t* index, int64_t n,
+                                             int32_t scatter, const attn_tensor* dst) {
+  attn::PermuteParams P;
+  return prepare_permute(src, index, n, scatter, dst, &P);
+}
+
+ATTN_API int attn_sink_cp_permute_rows(const attn_tensor* src, const int64_t* index, int64_t n, int32_t scatter,
+                                       const attn_tensor* dst, hipStream_t stream) {
+  attn::PermuteParams P;
+  const int rc = prepare_permute(src, index, n, scatter, dst, &P);
+  if (rc != ATTN_OK || P.n == 0 || P.chunks == 0) return rc;
+  return attn::launch_permute_rows(P, stream) == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+ATTN_API int attn_sink_cp_documents_check(const int64_t* positions, int64_t T, const int32_t* doc_ids,
+                                          const int32_t* cu_seqlens, int32_t max_docs, const int32_t* num_docs) {
+  attn::CpDocParams P;
+  return prepare_cp_documents(positions, T, doc_ids, cu_seqlens, max_docs, num_docs, &P);
+}
+
+ATTN_API int attn_sink_cp_documents(const int64_t* positions, int64_t T, int32_t* doc_ids, int32_t* cu_seqlens,
+                                    int32_t max_docs, int32_t* num_docs, hipStream_t stream) {
+  attn::CpDocParams P;
+  const int rc = prepare_cp_documents(positions, T, doc_ids, cu_seqlens, max_docs, num_docs, &P);
+  if (rc != ATTN_OK) return rc;
+  if (!doc_ids && !cu_seqlens && !num_docs) return ATTN_OK;
+  return attn::launch_cp_documents(P, stream) == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
 ATTN_API const char* attn_sink_strerror(int status) {

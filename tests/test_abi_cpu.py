@@ -243,3 +243,43 @@ def test_merge_validation(sam):
     b = merge_args()
     b["lse"] = b["parts"][0][1]
     assert sam.STATUS[merge_check(sam, b)] == "ATTN_ERR_RANGE"
+
+
+# ------------------------------------------------ context-parallel reorder
+def test_cp_validation(sam):
+    slots = torch.empty(64, dtype=torch.int64)
+    assert sam.attn_sink_cp_slots_check(4, 16, -1, slots) == 0
+    assert sam.attn_sink_cp_slots_check(4, 16, 3, slots) == 0
+    assert sam.attn_sink_cp_slots_check(1, 0, 0, None) == 0
+    for args, expect in (((0, 16, -1, slots), "ATTN_ERR_RANGE"), ((4, 15, -1, slots), "ATTN_ERR_RANGE"),
+                         ((4, 16, 4, slots), "ATTN_ERR_RANGE"), ((4, 16, -2, slots), "ATTN_ERR_RANGE"),
+                         ((4, 16, -1, None), "ATTN_ERR_NULL")):
+        assert sam.STATUS[sam.attn_sink_cp_slots_check(*args)] == expect, (args[:3], expect)
+
+    src = torch.empty(32, 8, 128, dtype=torch.bfloat16)
+    dst = torch.empty(32, 8, 128, dtype=torch.bfloat16)
+    idx = torch.empty(32, dtype=torch.int64)
+    chk = sam.attn_sink_cp_permute_rows_check
+    assert chk(src, idx, 32, 1, dst) == 0 and chk(src, idx, 32, 0, dst) == 0
+    assert chk(torch.empty(32, dtype=torch.int64), idx, 32, 1, torch.empty(32, dtype=torch.int64)) == 0
+    assert chk(torch.empty(10, 3, dtype=torch.int32), idx[:10], 10, 0, torch.empty(10, 3, dtype=torch.int32)) == 0
+    assert chk(src, idx[:20], 20, 0, torch.empty(20, 8, 128, dtype=torch.bfloat16)) == 0  # gather a subset
+    for over, expect in (({"scatter": 2}, "ATTN_ERR_ENUM"), ({"index": None}, "ATTN_ERR_NULL"),
+                         ({"dst": torch.empty(32, 8, 128, dtype=torch.float32)}, "ATTN_ERR_DTYPE"),
+                         ({"dst": torch.empty(32, 8, 64, dtype=torch.bfloat16)}, "ATTN_ERR_SHAPE"),
+                         ({"n": 31}, "ATTN_ERR_SHAPE"), ({"dst": src}, "ATTN_ERR_RANGE"),
+                         ({"src": torch.empty(32, 128, 8, dtype=torch.bfloat16).transpose(1, 2)}, "ATTN_ERR_STRIDE"),
+                         ({"src": torch.empty(32, 3, dtype=torch.uint8), "dst": torch.empty(32, 3, dtype=torch.uint8)},
+                          "ATTN_ERR_UNSUPPORTED")):
+        a = dict(src=src, index=idx, n=32, scatter=1, dst=dst)
+        a.update(over)
+        assert sam.STATUS[chk(a["src"], a["index"], a["n"], a["scatter"], a["dst"])] == expect, (over.keys(), expect)
+
+    pos = torch.empty(100, dtype=torch.int64)
+    ids, cu, nd = torch.empty(100, dtype=torch.int32), torch.empty(9, dtype=torch.int32), torch.empty(1, dtype=torch.int32)
+    dchk = sam.attn_sink_cp_documents_check
+    assert dchk(pos, 100, ids, cu, 8, nd) == 0 and dchk(pos, 100, None, None, 0, None) == 0
+    assert dchk(None, 0, None, cu, 8, nd) == 0
+    assert sam.STATUS[dchk(None, 100, ids, cu, 8, nd)] == "ATTN_ERR_NULL"
+    assert sam.STATUS[dchk(pos, -1, ids, cu, 8, nd)] == "ATTN_ERR_RANGE"
+    assert sam.STATUS[dchk(pos, 100, ids, cu, -1, nd)] == "ATTN_ERR_RANGE"
