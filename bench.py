@@ -16,6 +16,7 @@ kernel + closed-form key-0 correction); --measure-merge (mla_topk) times the
 top-k lists split in two halves, each through the no-sink kernel, merged by LSE
 with the sink folded in after the merge; --measure-cp (blocksparse_32k) times the
 context-parallel reorder of K/V from an 8-rank load-balanced layout.
+--workload mla_decode_fp8 times the sparse-MLA decode over an fp8 latent cache.
 
 Prints ONE JSON line:
   value      useful TFLOP/s of the whole job = 2 (Dqk + Dv) sum |S(i,h)| / wall time
@@ -386,13 +387,88 @@ def cpu_baseline(case, pairs_row, dqk_dv, budget_s, out_dev, lse_dev):
         {"max_rel_l2": rel, "lse_max_abs": dl, "rows_checked": n}
 
 
+def bench_decode(args, case):
+    """The fp8 sparse-MLA decode: two launches per step (list pieces, then the
+    LSE merge with the sink), inputs rotated over enough sets to exceed the
+    Infinity Cache.  Useful FLOPs count valid (row, key) pairs only; the
+    algorithmic bytes are q, out, lse, every distinct cache row touched
+    (576 fp8 bytes + its fp32 scale), the index lists and the sinks."""
+    import torch
+    import sink_aware_masked_amd as sam
+    idx = case["topk_idx"]
+    T, Hq = case["q"].shape[:2]
+    Tk = case["kv_fp8"].shape[0]
+    valid = (idx >= 0) & (idx < Tk)
+    prow = valid.sum(1).astype(np.int64) * Hq
+    F = 2.0 * (576 + 512) * float(prow.sum())
+    distinct = np.unique(idx[valid]).size
+    B = int(T * Hq * 576 * 2 + T * Hq * 512 * 2 + Hq * T * 4 + distinct * (576 + 4) + idx.nbytes + Hq * 4)
+    one = B + int(case["kv_fp8"].nbytes) - distinct * 576  # the whole cache is resident per set
+    sets_n = args.sets or max(1, min(16, math.ceil(1.25 * MALL_BYTES / one)))
+    log(f"[bench] decode: useful FLOPs {F:.4e}, algorithmic bytes {B:.4e}, sets {sets_n}")
+    sets = [sam.decode_case_on_device(case, "cuda:0") for _ in range(sets_n)]
+    counter = [0]
+
+    def step():
+        d = sets[counter[0] % sets_n]
+        counter[0] += 1
+        sam.attn_sink_mla_decode_fp8(d["q"], d["kv"], d["kv_scale"], d["topk_idx"], d["sinks"], d["sink_mode"],
+                                     d["scale"], d["out"], d["lse"], d["workspace"])
+    t0 = time.perf_counter()
+    kern_ms = graph_ms(step, args.steps, args.warmup)
+    ms = kern_ms  # the graph replay is the whole timed job
+    ach = F / (kern_ms * 1e-3) / 1e12
+    res = {"metric": METRIC, "value": F / (ms * 1e-3) / 1e12, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16 (fp8 e4m3 cache)", "data": "synthetic",
+           "config": {"workload": "mla_decode_fp8", "rows": int(T), "q_heads": int(Hq), "kv_entries": int(Tk),
+                      "topk": int(idx.shape[1]), "head_dim_qk": 576, "head_dim_v": 512, "cache": "fp8 e4m3 + fp32 row scale",
+                      "sink_mode": case["sink_mode"], "cold_cache_sets": sets_n},
+           "roofline": {"bound": "mfma", "achieved": ach, "peak": PEAK_MFMA_BF16_TFS, "unit": "TFLOP/s",
+                        "frac": ach / PEAK_MFMA_BF16_TFS, "traffic": None, "kernel_ms": kern_ms,
+                        "algorithmic_bytes": B, "useful_flops": F,
+                        "hbm_GBps": B / (kern_ms * 1e-3) / 1e9},
+           "wall_s": time.perf_counter() - t0}
+    d = sets[0]
+    sam.attn_sink_mla_decode_fp8(d["q"], d["kv"], d["kv_scale"], d["topk_idx"], d["sinks"], d["sink_mode"],
+                                 d["scale"], d["out"], d["lse"], d["workspace"])
+    torch.cuda.synchronize()
+    if args.cpu_seconds > 0:
+        from oracle import fp8
+        g = np.random.default_rng(1234)
+        rows = np.sort(g.choice(T, size=min(T, 8), replace=False))
+        reps, secs = 0, 0.0
+        while secs < 0.8 * args.cpu_seconds and reps < 100:
+            t = time.perf_counter()
+            ref_o, ref_l = fp8.decode_ref(case, rows=rows)
+            secs += time.perf_counter() - t
+            reps += 1
+        import oracle
+        flops = 2.0 * 1088 * float(prow[rows].sum()) * reps
+        out = d["out"].float().cpu().numpy().astype(np.float64)[rows]
+        num = np.linalg.norm(out - ref_o, axis=2)
+        den = np.linalg.norm(ref_o, axis=2)
+        nz = den > 0
+        res["cpu_baseline"] = {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+                               "kind": "oracle",
+                               "sample": f"{len(rows)} of {T} rows (all heads), seeded, x{reps} passes; {secs:.1f} s wall; "
+                                         "fp64 C enumerator after an fp64 NumPy dequantization of the cache"}
+        res["parity_sample"] = {"max_rel_l2": float((num[nz] / den[nz]).max()),
+                                "lse_max_abs": float(np.abs(d["lse"].cpu().numpy()[:, rows] - ref_l).max()),
+                                "rows_checked": int(len(rows))}
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="window_4k",
-                    choices=["window_4k", "window_16k", "mla_topk", "blocksparse_32k"])
+                    choices=["window_4k", "window_16k", "mla_topk", "blocksparse_32k", "mla_decode_fp8"])
     ap.add_argument("--sink-mode", default=None, choices=[None, "none", "key0_bias", "null_logit"])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--sets", type=int, default=0, help="input sets to rotate (0: enough to exceed the MALL)")
@@ -426,6 +502,8 @@ def main(argv=None):
 
     log(f"[bench] building workload {args.workload} seed {args.seed}")
     case = build_case(args.workload, args.seed, args.sink_mode)
+    if case["mask_kind"] == "topk_fp8":
+        return bench_decode(args, case)
     prow = pairs_per_row(case)
     dqk, dv = case["q"].shape[2], case["v"].shape[2]
     F = 2.0 * (dqk + dv) * float(prow.sum())

@@ -39,13 +39,14 @@
  *   - Strides are in elements.  The innermost dimension of q, k, v and out must
  *     be contiguous (stride 1); the other strides are free but must keep every
  *     row 16-byte aligned (bf16: multiples of 8 elements; f32: of 4).
- *   - The caller owns every buffer.  The library allocates nothing and keeps no
+ *   - The caller owns every buffer, including the one scratch buffer (the fp8
+ *     decode's workspace).  The library allocates nothing and keeps no
  *     mutable global state: calls are reentrant and may run concurrently on
  *     different streams.  Inputs are read only.  attn_sink_fwd and
  *     attn_sink_merge fully write out and lse (rows with an empty key set get
  *     out = 0 and lse = -inf); attn_sink_key0_correct updates them in place.
- *   - Each call enqueues a single kernel launch on `stream`; no call ever
- *     synchronises or reads device memory from the host.
+ *   - Each call enqueues a single kernel launch on `stream` (the fp8 decode
+ *     two); no call ever synchronises or reads device memory from the host.
  *   - Errors are returned as negative attn_status codes.  Every argument error
  *     is detected on the host BEFORE anything is enqueued.  Device-side data
  *     (cu_seqlens contents, indices) is not validated -- see the
@@ -98,7 +99,8 @@ typedef enum attn_dtype {
   ATTN_DTYPE_F32 = 1,
   ATTN_DTYPE_I32 = 2,
   ATTN_DTYPE_U8 = 3,
-  ATTN_DTYPE_I64 = 4   /* position ids / slot indices (context-parallel reorder) */
+  ATTN_DTYPE_I64 = 4,  /* position ids / slot indices (context-parallel reorder) */
+  ATTN_DTYPE_FP8_E4M3 = 5  /* OCP fp8 e4m3 (bias 7, max 448, no inf); fp8 latent cache */
 } attn_dtype;
 
 typedef enum attn_status {
@@ -319,6 +321,46 @@ int attn_sink_cp_documents(const int64_t* positions, int64_t T, int32_t* doc_ids
                            int32_t max_docs, int32_t* num_docs, hipStream_t stream);
 int attn_sink_cp_documents_check(const int64_t* positions, int64_t T, const int32_t* doc_ids,
                                  const int32_t* cu_seqlens, int32_t max_docs, const int32_t* num_docs);
+
+/*
+ * attn_sink_mla_decode_fp8 -- sparse-MLA decode over an fp8 latent KV cache
+ * (the decode call site of "Apply DeepSeek-V4 attn_sink in the XPU sparse-MLA
+ * Triton kernel"; the sink fold of its Implementation paragraph).  For every
+ * query row i and head h, with K[j] = fp8(kv[j, 0, :]) * kv_scale[j] (576
+ * values) and V[j] = the first 512 of them:
+ *     out[i, h, :] = sum_j e^{l_j} V[j] / (sum_j e^{l_j} [+ e^{sinks[h]}])
+ *     l_j = scale * q[i, h, :] . K[j]  over the valid entries of topk_idx[i, :]
+ *     lse[h, i] = log sum_j e^{l_j}  (selected keys only)
+ * The page names the fp8 cache but not its encoding; this entry point reads
+ * it as OCP e4m3 values, 576 per row, with one fp32 scale per row.
+ *   q          bf16 [T, Hq, 576], Hq a multiple of 64
+ *   kv         ATTN_DTYPE_FP8_E4M3 [Tk, 1, 576]; row stride a multiple of 16 B
+ *   kv_scale   device f32 [Tk]
+ *   topk_idx   int32 [T, topk]; entries outside [0, Tk) are padding
+ *   sink_mode  ATTN_SINK_NONE or ATTN_SINK_NULL_LOGIT (sinks: device f32 [Hq])
+ *   out        bf16 [T, Hq, 512];  lse: device f32 [Hq, T]
+ *   workspace  device memory of at least the size reported by
+ *              attn_sink_mla_decode_fp8_workspace for (T, Hq, topk), 16-byte
+ *              aligned; caller-owned scratch, overwritten by every call, so
+ *              calls that share a workspace must not run concurrently
+ * Few query rows leave the GPU idle, so each row's list is cut into pieces
+ * computed by separate workgroups (fp32 partial results in the workspace) and
+ * a second kernel merges them and folds the sink in once: two kernel launches
+ * on `stream`.  Errors as for attn_sink_fwd; ATTN_ERR_RANGE for a workspace
+ * that is too small.
+ */
+int attn_sink_mla_decode_fp8(const attn_tensor* q, const attn_tensor* kv, const float* kv_scale,
+                             const attn_tensor* topk_idx, const float* sinks, int32_t sink_mode, float scale,
+                             const attn_tensor* out, float* lse, void* workspace, int64_t workspace_bytes,
+                             hipStream_t stream);
+int attn_sink_mla_decode_fp8_check(const attn_tensor* q, const attn_tensor* kv, const float* kv_scale,
+                                   const attn_tensor* topk_idx, const float* sinks, int32_t sink_mode, float scale,
+                                   const attn_tensor* out, const float* lse, const void* workspace,
+                                   int64_t workspace_bytes);
+/* Workspace bytes attn_sink_mla_decode_fp8 needs for T rows, Hq heads and
+ * top-k lists of length topk (host-only; ATTN_ERR_RANGE if Hq is not a
+ * positive multiple of 64). */
+int attn_sink_mla_decode_fp8_workspace(int64_t T, int64_t Hq, int64_t topk, int64_t* bytes);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* attn_sink_strerror(int status);

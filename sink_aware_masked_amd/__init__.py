@@ -25,14 +25,15 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 MASK_KINDS = {"window": 0, "topk": 1, "blocksel": 2}
 SINK_MODES = {"none": 0, "key0_bias": 1, "null_logit": 2}
-DTYPE_BF16, DTYPE_F32, DTYPE_I32, DTYPE_U8, DTYPE_I64 = 0, 1, 2, 3, 4
+DTYPE_BF16, DTYPE_F32, DTYPE_I32, DTYPE_U8, DTYPE_I64, DTYPE_FP8_E4M3 = 0, 1, 2, 3, 4, 5
 STATUS = {0: "ATTN_OK", -1: "ATTN_ERR_NULL", -2: "ATTN_ERR_ENUM", -3: "ATTN_ERR_SHAPE",
           -4: "ATTN_ERR_STRIDE", -5: "ATTN_ERR_HEADS", -6: "ATTN_ERR_DTYPE",
           -7: "ATTN_ERR_UNSUPPORTED", -8: "ATTN_ERR_RANGE", -9: "ATTN_ERR_LAUNCH"}
 EXPORTS = ("attn_sink_fwd", "attn_sink_check", "attn_sink_key0_correct", "attn_sink_key0_correct_check",
            "attn_sink_merge", "attn_sink_merge_check", "attn_sink_cp_slots", "attn_sink_cp_slots_check",
            "attn_sink_cp_permute_rows", "attn_sink_cp_permute_rows_check", "attn_sink_cp_documents",
-           "attn_sink_cp_documents_check", "attn_sink_strerror", "attn_sink_abi_version")
+           "attn_sink_cp_documents_check", "attn_sink_mla_decode_fp8", "attn_sink_mla_decode_fp8_check",
+           "attn_sink_mla_decode_fp8_workspace", "attn_sink_strerror", "attn_sink_abi_version")
 MERGE_MAX_PARTS = 8
 
 
@@ -79,6 +80,13 @@ _lib.attn_sink_cp_documents.restype = ctypes.c_int
 _lib.attn_sink_cp_documents.argtypes = [_P, _I64, _P, _P, _I32, _P, _P]
 _lib.attn_sink_cp_documents_check.restype = ctypes.c_int
 _lib.attn_sink_cp_documents_check.argtypes = [_P, _I64, _P, _P, _I32, _P]
+_DEC = [_T, _T, _P, _T, _P, _I32, ctypes.c_float, _T, _P, _P, _I64]
+_lib.attn_sink_mla_decode_fp8.restype = ctypes.c_int
+_lib.attn_sink_mla_decode_fp8.argtypes = _DEC + [_P]
+_lib.attn_sink_mla_decode_fp8_check.restype = ctypes.c_int
+_lib.attn_sink_mla_decode_fp8_check.argtypes = _DEC
+_lib.attn_sink_mla_decode_fp8_workspace.restype = ctypes.c_int
+_lib.attn_sink_mla_decode_fp8_workspace.argtypes = [_I64, _I64, _I64, ctypes.POINTER(ctypes.c_int64)]
 _lib.attn_sink_strerror.restype = ctypes.c_char_p
 _lib.attn_sink_strerror.argtypes = [ctypes.c_int]
 _lib.attn_sink_abi_version.restype = ctypes.c_int
@@ -102,7 +110,8 @@ def attn_sink_abi_version() -> int:
 def _dtype_code(t) -> int:
     import torch
     codes = {torch.bfloat16: DTYPE_BF16, torch.float32: DTYPE_F32, torch.int32: DTYPE_I32,
-             torch.uint8: DTYPE_U8, torch.bool: DTYPE_U8, torch.int64: DTYPE_I64}
+             torch.uint8: DTYPE_U8, torch.bool: DTYPE_U8, torch.int64: DTYPE_I64,
+             torch.float8_e4m3fn: DTYPE_FP8_E4M3}
     if t.dtype not in codes:
         raise TypeError(f"unsupported tensor dtype {t.dtype}")
     return codes[t.dtype]
@@ -333,6 +342,53 @@ def attn_sink_cp_documents(positions, doc_ids=None, cu_seqlens=None, num_docs=No
     _check_rc(_lib.attn_sink_cp_documents(_ptr(positions), int(positions.numel()), _ptr(doc_ids),
                                           _ptr(cu_seqlens), int(max_docs), _ptr(num_docs),
                                           ctypes.c_void_p(_stream(stream, positions.device))))
+
+
+def attn_sink_mla_decode_fp8_workspace(T, Hq, topk) -> int:
+    """Workspace bytes the fp8 decode needs (host-only)."""
+    n = ctypes.c_int64(0)
+    _check_rc(_lib.attn_sink_mla_decode_fp8_workspace(int(T), int(Hq), int(topk), ctypes.byref(n)))
+    return int(n.value)
+
+
+def attn_sink_mla_decode_fp8_check(q, kv, kv_scale, topk_idx, sinks, sink_mode, scale, out, lse, workspace,
+                                   workspace_bytes) -> int:
+    sm = SINK_MODES[sink_mode] if isinstance(sink_mode, str) else int(sink_mode)
+    dq, dk, di, do = (_as_desc(x) for x in (q, kv, topk_idx, out))
+    return int(_lib.attn_sink_mla_decode_fp8_check(_ref(dq), _ref(dk), _ptr(kv_scale), _ref(di), _ptr(sinks), sm,
+                                                   float(scale), _ref(do), _ptr(lse), _ptr(workspace),
+                                                   int(workspace_bytes)))
+
+
+def attn_sink_mla_decode_fp8(q, kv, kv_scale, topk_idx, sinks, sink_mode, scale, out, lse, workspace,
+                             stream=None) -> None:
+    """Sparse-MLA decode over an fp8 e4m3 latent cache kv [Tk, 1, 576] with
+    per-row fp32 scales; workspace: a device tensor of at least
+    attn_sink_mla_decode_fp8_workspace(T, Hq, topk) bytes."""
+    sm = SINK_MODES[sink_mode] if isinstance(sink_mode, str) else int(sink_mode)
+    dq, dk, di, do = desc(q), desc(kv), desc(topk_idx), desc(out)
+    nbytes = workspace.numel() * workspace.element_size()
+    _check_rc(_lib.attn_sink_mla_decode_fp8(ctypes.byref(dq), ctypes.byref(dk), _ptr(kv_scale), ctypes.byref(di),
+                                            _ptr(sinks), sm, float(scale), ctypes.byref(do), _ptr(lse),
+                                            _ptr(workspace), int(nbytes), ctypes.c_void_p(_stream(stream, q.device))))
+
+
+def decode_case_on_device(case: dict, device="cuda:0") -> dict:
+    """Device tensors of a generated fp8 decode case (fp8 bytes viewed as
+    torch.float8_e4m3fn) plus out / lse / workspace buffers."""
+    import torch
+    T, Hq = case["q"].shape[:2]
+    topk = case["topk_idx"].shape[1]
+    d = dict(q=torch.from_numpy(case["q"]).to(device=device, dtype=torch.bfloat16),
+             kv=torch.from_numpy(case["kv_fp8"]).to(device).view(torch.float8_e4m3fn),
+             kv_scale=torch.from_numpy(case["kv_scale"]).to(device),
+             topk_idx=torch.from_numpy(case["topk_idx"]).to(device),
+             sinks=None if case["sinks"] is None else torch.from_numpy(case["sinks"]).to(device),
+             sink_mode=case["sink_mode"], scale=case["scale"])
+    d["out"] = torch.empty((T, Hq, 512), dtype=torch.bfloat16, device=device)
+    d["lse"] = torch.empty((Hq, T), dtype=torch.float32, device=device)
+    d["workspace"] = torch.empty(attn_sink_mla_decode_fp8_workspace(T, Hq, topk), dtype=torch.uint8, device=device)
+    return d
 
 
 def case_on_device(case: dict, device="cuda:0") -> dict:

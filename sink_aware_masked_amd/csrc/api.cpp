@@ -10,6 +10,7 @@
 #include "common.hpp"
 #include "compose.hpp"
 #include "cp.hpp"
+#include "decode.hpp"
 
 #define ATTN_API extern "C" __attribute__((visibility("default")))
 
@@ -37,11 +38,12 @@ int elem_size(int32_t dt) {
     case ATTN_DTYPE_I32: return 4;
     case ATTN_DTYPE_U8: return 1;
     case ATTN_DTYPE_I64: return 8;
+    case ATTN_DTYPE_FP8_E4M3: return 1;
     default: return 0;
   }
 }
 
-bool valid_dtype(int32_t dt) { return dt >= ATTN_DTYPE_BF16 && dt <= ATTN_DTYPE_I64; }
+bool valid_dtype(int32_t dt) { return dt >= ATTN_DTYPE_BF16 && dt <= ATTN_DTYPE_FP8_E4M3; }
 
 // Rank, non-negative sizes / strides, unit inner stride.
 // A NULL data pointer is accepted only for an empty tensor.
@@ -490,6 +492,86 @@ ATTN_API int attn_sink_cp_documents(const int64_t* positions, int64_t T, int32_t
   if (rc != ATTN_OK) return rc;
   if (!doc_ids && !cu_seqlens && !num_docs) return ATTN_OK;
   return attn::launch_cp_documents(P, stream) == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+namespace {
+
+// ---------------------------------------------------------------- fp8 sparse-MLA decode
+int64_t decode_ws_bytes(int64_t T, int64_t Hq, int nsplit) {
+  return (int64_t)nsplit * T * Hq * (512 * 4 + 4);
+}
+
+int prepare_decode(const attn_tensor* q, const attn_tensor* kv, const float* kv_scale, const attn_tensor* ti,
+                   const float* sinks, int32_t sink_mode, float scale, const attn_tensor* out, const float* lse,
+                   const void* ws, int64_t ws_bytes, attn::DecodeParams* P) {
+  if (!q || !kv || !ti || !out) return ATTN_ERR_NULL;
+  if (sink_mode < ATTN_SINK_NONE || sink_mode > ATTN_SINK_NULL_LOGIT) return ATTN_ERR_ENUM;
+  if (sink_mode == ATTN_SINK_KEY0_BIAS) return ATTN_ERR_UNSUPPORTED;
+  if (sink_mode == ATTN_SINK_NULL_LOGIT && !sinks) return ATTN_ERR_NULL;
+  int rc;
+  if ((rc = check_tensor(q, 3)) || (rc = check_tensor(kv, 3)) || (rc = check_tensor(out, 3)) ||
+      (rc = check_tensor(ti, 2)))
+    return rc;
+  if (q->dtype != ATTN_DTYPE_BF16 || out->dtype != ATTN_DTYPE_BF16 || kv->dtype != ATTN_DTYPE_FP8_E4M3 ||
+      ti->dtype != ATTN_DTYPE_I32)
+    return ATTN_ERR_DTYPE;
+  const int64_t T = q->shape[0], Hq = q->shape[1], Tk = kv->shape[0];
+  if (q->shape[2] != 576 || kv->shape[1] != 1 || kv->shape[2] != 576 || out->shape[2] != 512)
+    return ATTN_ERR_UNSUPPORTED;
+  if (out->shape[0] != T || out->shape[1] != Hq || ti->shape[0] != T) return ATTN_ERR_SHAPE;
+  if (Hq < 64 || Hq % 64 != 0) return ATTN_ERR_UNSUPPORTED;
+  if (T > kMaxTokens || Tk > kMaxTokens || ti->shape[1] > kMaxTokens || Hq > 65535) return ATTN_ERR_RANGE;
+  if ((rc = check_rows_aligned(q)) || (rc = check_rows_aligned(out))) return rc;
+  if (reinterpret_cast<uintptr_t>(kv->data) % 16 != 0 || kv->stride[0] % 16 != 0) return ATTN_ERR_STRIDE;
+  if (Tk > 1 && kv->stride[0] < 576) return ATTN_ERR_STRIDE;
+  if (Tk > 0 && !kv_scale) return ATTN_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(kv_scale) % 4 != 0 || reinterpret_cast<uintptr_t>(ti->data) % 4 != 0)
+    return ATTN_ERR_STRIDE;
+  if (!lse && T > 0) return ATTN_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(lse) % 4 != 0) return ATTN_ERR_STRIDE;
+  if (!(scale == scale) || scale == __builtin_huge_valf() || scale == -__builtin_huge_valf()) return ATTN_ERR_RANGE;
+  const int nsplit = attn::decode_splits(T, Hq, ti->shape[1]);
+  if (T > 0 && (!ws || ws_bytes < decode_ws_bytes(T, Hq, nsplit))) return ws ? ATTN_ERR_RANGE : ATTN_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(ws) % 16 != 0) return ATTN_ERR_STRIDE;
+  memset(P, 0, sizeof(*P));
+  P->q = q->data; P->k = kv->data; P->kv_scale = kv_scale; P->topk_idx = static_cast<const int32_t*>(ti->data);
+  P->sinks = sinks; P->out = out->data; P->lse = const_cast<float*>(lse);
+  P->ws_out = static_cast<float*>(const_cast<void*>(ws));
+  P->ws_lse = P->ws_out + (int64_t)nsplit * T * Hq * 512;
+  P->q_row = q->stride[0]; P->q_head = q->stride[1]; P->k_row = kv->stride[0];
+  P->o_row = out->stride[0]; P->o_head = out->stride[1]; P->topk_row = ti->stride[0];
+  P->T = (int)T; P->Tk = (int)Tk; P->Hq = (int)Hq; P->topk = (int)ti->shape[1];
+  P->nsplit = nsplit; P->split_len = attn::decode_split_len(ti->shape[1], nsplit);
+  P->scale_log2 = scale * attn::kLog2e;
+  return ATTN_OK;
+}
+
+}  // namespace
+
+ATTN_API int attn_sink_mla_decode_fp8_workspace(int64_t T, int64_t Hq, int64_t topk, int64_t* bytes) {
+  if (!bytes) return ATTN_ERR_NULL;
+  if (T < 0 || Hq < 64 || Hq % 64 != 0 || topk < 0 || T > kMaxTokens || topk > kMaxTokens) return ATTN_ERR_RANGE;
+  *bytes = decode_ws_bytes(T, Hq, attn::decode_splits(T, Hq, topk));
+  return ATTN_OK;
+}
+
+ATTN_API int attn_sink_mla_decode_fp8_check(const attn_tensor* q, const attn_tensor* kv, const float* kv_scale,
+                                            const attn_tensor* topk_idx, const float* sinks, int32_t sink_mode,
+                                            float scale, const attn_tensor* out, const float* lse,
+                                            const void* workspace, int64_t workspace_bytes) {
+  attn::DecodeParams P;
+  return prepare_decode(q, kv, kv_scale, topk_idx, sinks, sink_mode, scale, out, lse, workspace, workspace_bytes, &P);
+}
+
+ATTN_API int attn_sink_mla_decode_fp8(const attn_tensor* q, const attn_tensor* kv, const float* kv_scale,
+                                      const attn_tensor* topk_idx, const float* sinks, int32_t sink_mode,
+                                      float scale, const attn_tensor* out, float* lse, void* workspace,
+                                      int64_t workspace_bytes, hipStream_t stream) {
+  attn::DecodeParams P;
+  const int rc = prepare_decode(q, kv, kv_scale, topk_idx, sinks, sink_mode, scale, out, lse, workspace,
+                                workspace_bytes, &P);
+  if (rc != ATTN_OK || P.T == 0) return rc;
+  return attn::launch_mla_decode_fp8(P, sink_mode, stream) == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
 ATTN_API const char* attn_sink_strerror(int status) {

@@ -283,3 +283,42 @@ def test_cp_validation(sam):
     assert sam.STATUS[dchk(None, 100, ids, cu, 8, nd)] == "ATTN_ERR_NULL"
     assert sam.STATUS[dchk(pos, -1, ids, cu, 8, nd)] == "ATTN_ERR_RANGE"
     assert sam.STATUS[dchk(pos, 100, ids, cu, -1, nd)] == "ATTN_ERR_RANGE"
+
+
+# ------------------------------------------------------------ fp8 decode
+def decode_args(T=8, Hq=64, Tk=100, topk=32):
+    return dict(q=torch.empty(T, Hq, 576, dtype=torch.bfloat16),
+                kv=torch.empty(Tk, 1, 576, dtype=torch.float8_e4m3fn), kv_scale=torch.empty(Tk),
+                topk_idx=torch.empty(T, topk, dtype=torch.int32), sinks=torch.zeros(Hq), sink_mode="null_logit",
+                scale=0.04, out=torch.empty(T, Hq, 512, dtype=torch.bfloat16), lse=torch.empty(Hq, T))
+
+
+def decode_check(sam, a, ws_bytes=None):
+    T, Hq, topk = a["q"].shape[0], a["q"].shape[1], a["topk_idx"].shape[1]
+    need = sam.attn_sink_mla_decode_fp8_workspace(T, Hq, topk) if Hq % 64 == 0 and Hq > 0 else 16
+    ws = torch.empty(max(need, 16), dtype=torch.uint8)
+    return sam.attn_sink_mla_decode_fp8_check(a["q"], a["kv"], a["kv_scale"], a["topk_idx"], a["sinks"], a["sink_mode"],
+                                              a["scale"], a["out"], a["lse"], ws,
+                                              need if ws_bytes is None else ws_bytes)
+
+
+def test_decode_validation(sam):
+    assert sam.attn_sink_mla_decode_fp8_workspace(128, 64, 2048) > 0
+    assert decode_check(sam, decode_args()) == 0
+    a = decode_args()
+    a.update(sink_mode="none", sinks=None)
+    assert decode_check(sam, a) == 0
+    assert decode_check(sam, decode_args(Hq=128)) == 0
+    for over, expect in (({"sink_mode": "key0_bias"}, "ATTN_ERR_UNSUPPORTED"), ({"sinks": None}, "ATTN_ERR_NULL"),
+                         ({"kv": torch.empty(100, 1, 576, dtype=torch.bfloat16)}, "ATTN_ERR_DTYPE"),
+                         ({"kv": torch.empty(100, 1, 512, dtype=torch.float8_e4m3fn)}, "ATTN_ERR_UNSUPPORTED"),
+                         ({"kv_scale": None}, "ATTN_ERR_NULL"),
+                         ({"out": torch.empty(8, 64, 576, dtype=torch.bfloat16)}, "ATTN_ERR_UNSUPPORTED"),
+                         ({"topk_idx": torch.empty(9, 32, dtype=torch.int32)}, "ATTN_ERR_SHAPE"),
+                         ({"scale": float("nan")}, "ATTN_ERR_RANGE")):
+        b = decode_args()
+        b.update(over)
+        assert sam.STATUS[decode_check(sam, b)] == expect, (over.keys(), expect)
+    assert sam.STATUS[decode_check(sam, decode_args(), ws_bytes=64)] == "ATTN_ERR_RANGE"
+    b = decode_args(Hq=32)
+    assert sam.STATUS[decode_check(sam, b)] == "ATTN_ERR_UNSUPPORTED"

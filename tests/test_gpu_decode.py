@@ -1,0 +1,71 @@
+"""GPU parity of the sparse-MLA decode over an fp8 latent cache (the decode
+call site of the DeepSeek-V4 XPU sparse-MLA page) against oracle/fp8.py:
+dequantized cache, top-k masked softmax, null-logit sink folded after the
+merge of the list pieces, LSE over the selected keys only."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import fp8
+from tests import gpu_util as G
+
+pytestmark = pytest.mark.gpu
+
+
+def run(case):
+    d = G.sam().decode_case_on_device(case)
+    G.sam().attn_sink_mla_decode_fp8(d["q"], d["kv"], d["kv_scale"], d["topk_idx"], d["sinks"], d["sink_mode"],
+                                     d["scale"], d["out"], d["lse"], d["workspace"])
+    torch.cuda.synchronize()
+    return d
+
+
+def check(case, label, rows=None):
+    d = run(case)
+    out = d["out"].float().cpu().numpy().astype(np.float64)
+    lse = d["lse"].cpu().numpy().astype(np.float64)
+    ref_o, ref_l = fp8.decode_ref(case, rows=rows)
+    if rows is not None:
+        out, lse = out[rows], lse[:, rows]
+    rel, dl = G.compare(out, lse, ref_o, ref_l)
+    G.say(f"[decode] {label}: max rel L2 {rel:.3e}, lse max abs {dl:.3e}")
+    assert rel <= G.BF16_REL_L2 and dl <= G.BF16_LSE_ABS, (rel, dl)
+    return d
+
+
+@pytest.mark.parametrize("T,Hq,topk,counts,kw", [
+    (1, 64, 2048, (2048,), {}),
+    (5, 64, 300, (0, 1, 17, 300), {"shuffled": True}),
+    (17, 128, 256, (1, 4, 16, 128, 256), {"shuffled": True, "out_of_range": True}),
+    (64, 64, 2048, (1, 4, 16, 128, 512, 2048), {}),
+    (300, 64, 512, (0, 33, 512), {"sink_mode": "none"}),
+])
+def test_decode_small(T, Hq, topk, counts, kw):
+    case = W.mla_decode_fp8_case(T, 5000, Hq, topk, counts=counts, seed=T + Hq, **kw)
+    check(case, f"T={T} Hq={Hq} topk={topk} {kw}")
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_decode_full_size(seed):
+    """The decode workload the benchmark times (128 rows x 64 heads, 65536-row
+    fp8 cache, full 2048-entry lists), every row against the oracle."""
+    check(W.make_workload("mla_decode_fp8", seed=seed), f"mla_decode_fp8 seed {seed}")
+
+
+def test_decode_full_size_buckets():
+    case = W.make_workload("mla_decode_fp8", seed=2, counts=(1, 4, 16, 128, 512, 2048), shuffled=True)
+    check(case, "mla_decode_fp8 buckets, shuffled padding")
+
+
+def test_decode_neg_inf_sink_is_bitwise_noop():
+    case = W.mla_decode_fp8_case(40, 3000, 64, 512, counts=(1, 9, 512), seed=9)
+    a = run(case)
+    case_inf = dict(case, sinks=np.full_like(case["sinks"], -np.inf))
+    b = run(case_inf)
+    none = run(dict(case, sink_mode="none", sinks=None))
+    assert torch.equal(b["out"], none["out"]) and torch.equal(b["lse"], none["lse"])
+    assert torch.equal(a["lse"], none["lse"])          # the LSE never includes the sink
+    assert not torch.equal(a["out"], none["out"])

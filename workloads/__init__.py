@@ -188,6 +188,31 @@ def blocksel_case(doc_lens, Hq: int, Hkv: int, D: int, *, block_size: int = 64, 
                 sink_mode=sink_mode, scale=float(1.0 / math.sqrt(D) if scale is None else scale))
 
 
+def mla_decode_fp8_case(T: int, Tk: int, Hq: int, topk: int, *, counts=(2048,), shuffled: bool = False,
+                        out_of_range: bool = False, sink_mode: str = "null_logit", sink_range=(-2.20, 2.49),
+                        std: float = 0.5, seed: int = 0, name: str = "mla_decode_fp8") -> dict:
+    """Decode rows over an fp8 latent cache: q bf16 N(0, std^2) [T, Hq, 576];
+    cache rows drawn N(0, std^2) in fp32, each stored as 576 fp8 e4m3 bytes
+    (round to nearest even, by torch's float8_e4m3fn conversion) with one fp32
+    scale per row, amax / 448 rounded up to an 8-bit mantissa (so scale times
+    any e4m3 value is exact in fp32).  Top-k lists as in topk_case."""
+    import torch
+    base = topk_case(T, Tk, Hq, 576, 512, topk, counts=counts, shuffled=shuffled, mla=True, std=std,
+                     sink_mode=sink_mode, sink_range=sink_range, seed=seed, out_of_range=out_of_range, name=name)
+    g = rng(50_000 + seed)
+    x = g.standard_normal((Tk, 576), dtype=np.float32) * np.float32(std)
+    amax = np.maximum(np.abs(x).max(axis=1), np.float32(1e-6))
+    sc = (amax / np.float32(448.0)).astype(np.float32)
+    bits = sc.view(np.uint32)
+    up = (bits & np.uint32(0xFFFF)) != 0
+    sc = ((bits & np.uint32(0xFFFF0000)) + (up.astype(np.uint32) << np.uint32(16))).view(np.float32)  # round up
+    q8 = torch.from_numpy(x / sc[:, None]).to(torch.float8_e4m3fn)
+    fp8 = q8.view(torch.uint8).numpy().reshape(Tk, 1, 576).copy()
+    base.update(kv_fp8=fp8, kv_scale=sc.astype(np.float32), k=None, v=None, v_aliases_k=True,
+                mask_kind="topk_fp8")
+    return base
+
+
 def c3_seqlens(seed: int, total: int = 16384, nseq: int = 8, W: int = 64) -> list[int]:
     """One length uniform in 1..W-1 (shorter than the window); the other nseq-1
     lengths from nseq-2 sorted uniform cut points over the remainder; the short
@@ -245,6 +270,10 @@ WORKLOADS = {
     # top-k 2048 with the page's valid-key buckets, sinks in [-2.20, 2.49].
     "mla_topk": lambda seed=0, sink_mode="null_logit", **kw: topk_case(
         4096, 65536, 64, 576, 512, 2048, sink_mode=sink_mode, seed=seed, name="mla_topk", **kw),
+    # Same page, decode call site: 128 decode rows x 64 heads over an fp8 latent
+    # cache of 65536 rows, full 2048-entry lists (steady-state decode).
+    "mla_decode_fp8": lambda seed=0, sink_mode="null_logit", **kw: mla_decode_fp8_case(
+        128, 65536, 64, 2048, sink_mode=sink_mode, seed=seed, **kw),
     # MiniMax-M3 CP sparse-attention page: block-sparse causal over 4 packed
     # documents, 32 q heads / 8 kv heads, head dim 128, 64-token key blocks.
     "blocksparse_32k": lambda seed=0, sink_mode="none": blocksel_case(
