@@ -132,16 +132,39 @@ void blocksel_fwd_bf16(const Params p) {
 
   // ---- stage one key block (K then V, this wave's LDPW 1-KB pieces of each);
   // rows past T re-read row T-1 (finite data; masked by causality).
+  // Per-lane element offsets of this wave's pieces inside a block: the
+  // block's first row is a wave-uniform 64-bit base, the rest 32-bit
+  // (a 64-row block spans less than 2^31 bytes).
+  int kpos[LDPW], vpos[LDPW];
+#pragma unroll
+  for (int u = 0; u < LDPW; ++u) {
+    const int i = wave * LDPW + u;  // 1-KB piece: line i >> 3 of rows 8 (i & 7) .. + 7
+    const int r = 8 * (i & 7) + (lane >> 3);
+    const int c = 8 * (8 * (i >> 3) + ((lane & 7) ^ (lane >> 3)));
+    kpos[u] = r * (int)p.k_row + c;
+    vpos[u] = r * (int)p.v_row + c;
+  }
   auto issue = [&](int blk, bf16* st) {
     const uint32_t base = lds_addr(st) + (uint32_t)(wave * LDPW * 1024);
+    const int64_t j0 = (int64_t)blk * BS;
+    if (j0 + BS <= p.T) {  // wave-uniform: every row of the block exists
+      const bf16* kb = kg + j0 * p.k_row;
+      const bf16* vb = vg + j0 * p.v_row;
 #pragma unroll
-    for (int u = 0; u < LDPW; ++u) {
-      const int i = wave * LDPW + u;  // 1-KB piece: line i >> 3 of rows 8 (i & 7) .. + 7
-      const int r = 8 * (i & 7) + (lane >> 3);
-      const int j = min(blk * BS + r, p.T - 1);
-      const int c = 8 * (8 * (i >> 3) + ((lane & 7) ^ (lane >> 3)));
-      load_lds16_m0(kg + (int64_t)j * p.k_row + c, base + u * 1024);
-      load_lds16_m0(vg + (int64_t)j * p.v_row + c, base + TILE_EL * 2 + u * 1024);
+      for (int u = 0; u < LDPW; ++u) {
+        load_lds16_m0(kb + kpos[u], base + u * 1024);
+        load_lds16_m0(vb + vpos[u], base + TILE_EL * 2 + u * 1024);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < LDPW; ++u) {
+        const int i = wave * LDPW + u;
+        const int r = 8 * (i & 7) + (lane >> 3);
+        const int j = min(blk * BS + r, p.T - 1);
+        const int c = 8 * (8 * (i >> 3) + ((lane & 7) ^ (lane >> 3)));
+        load_lds16_m0(kg + (int64_t)j * p.k_row + c, base + u * 1024);
+        load_lds16_m0(vg + (int64_t)j * p.v_row + c, base + TILE_EL * 2 + u * 1024);
+      }
     }
   };
 
@@ -175,7 +198,11 @@ void blocksel_fwd_bf16(const Params p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) s[sb][e] = a[e];
       }
-      if (edge) {  // wave-uniform: some selected column sees causality or a document start
+      // Elementwise masks only where some selected column sees causality or a
+      // document start (or the key-0 bias); otherwise a column's selection
+      // acts on the whole lane: the max below ignores it and the exponent
+      // takes scale 0 and offset -inf, which gives 0 for every finite logit.
+      if (edge) {  // wave-uniform
 #pragma unroll
         for (int sb = 0; sb < 4; ++sb)
 #pragma unroll
@@ -183,7 +210,7 @@ void blocksel_fwd_bf16(const Params p) {
             const int j = kb0 + 16 * sb + 4 * grp + e;
             s[sb][e] = (sel & (j <= qi[nb]) & (j >= dstart[nb])) ? s[sb][e] : kNegInf;
           }
-      } else {
+      } else if (has_key0) {
 #pragma unroll
         for (int sb = 0; sb < 4; ++sb)
 #pragma unroll
@@ -202,7 +229,7 @@ void blocksel_fwd_bf16(const Params p) {
         for (int sb = 0; sb < 4; ++sb)
 #pragma unroll
           for (int e = 0; e < 4; ++e) mt = fmaxf(mt, s[sb][e]);
-        mt *= sl2;  // sl2 > 0: the max commutes with the scaling
+        mt = sel ? mt * sl2 : kNegInf;  // sl2 > 0: the max commutes with the scaling
       }
       mt = max_over_groups(mt);
       if (__ballot(mt > m2[nb] + kRescaleLog2) != 0) {  // lazy rescale (wave-uniform)
@@ -225,11 +252,14 @@ void blocksel_fwd_bf16(const Params p) {
             ps += s[sb][e];
           }
       } else {
+        // masked elements are already -inf (scale sl2 keeps them so); on
+        // unmasked blocks an unselected column takes scale 0 and offset -inf
+        const float ks = (edge | sel) ? sl2 : 0.0f, ko = (edge | sel) ? -mu : kNegInf;
 #pragma unroll
         for (int sb = 0; sb < 4; ++sb)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            s[sb][e] = exp2f_fast(__builtin_fmaf(s[sb][e], sl2, -mu));
+            s[sb][e] = exp2f_fast(__builtin_fmaf(s[sb][e], ks, ko));
             ps += s[sb][e];
           }
       }
