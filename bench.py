@@ -468,7 +468,8 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="window_4k",
-                    choices=["window_4k", "window_16k", "mla_topk", "blocksparse_32k", "mla_decode_fp8"])
+                    choices=["window_4k", "window_16k", "mla_topk", "blocksparse_32k", "blocksparse_32k_coherent",
+                             "mla_decode_fp8"])
     ap.add_argument("--sink-mode", default=None, choices=[None, "none", "key0_bias", "null_logit"])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--sets", type=int, default=0, help="input sets to rotate (0: enough to exceed the MALL)")

@@ -24,6 +24,15 @@ def test_blocksparse_32k_sampled(seed, sink):
     G.assert_parity(case, rows=rows, label=f"blocksparse_32k {sink} seed{seed}")
 
 
+@pytest.mark.parametrize("sink", ["none", "null_logit"])
+def test_blocksparse_32k_coherent_sampled(sink):
+    """The labelled extra: the same layer with one selection per 64-query
+    block (shared by its queries); oracle on sampled rows."""
+    case = W.make_workload("blocksparse_32k_coherent", seed=0, sink_mode=sink)
+    rows = G.sample_rows(case, 300, seed=5)
+    G.assert_parity(case, rows=rows, label=f"blocksparse_32k_coherent {sink}")
+
+
 SMALL = [
     # (doc_lens, Hq, Hkv, Hidx, n_random, sink)
     ([300], 4, 1, 1, 2, "none"),

@@ -143,10 +143,14 @@ def topk_case(T: int, Tk: int, Hq: int, Dqk: int, Dv: int, topk: int, *, counts=
                 scale=float(1.0 / math.sqrt(Dqk) if scale is None else scale))
 
 
-def _block_table(g, doc_lens, Hidx: int, block_size: int, n_random: int) -> np.ndarray:
+def _block_table(g, doc_lens, Hidx: int, block_size: int, n_random: int, coherent: bool = False) -> np.ndarray:
     """[1, Hidx, T, NB] uint8: per (index head, query) the query's own block
     i // block_size plus min(n_random, c) distinct uniform picks among the c
-    earlier blocks that overlap the query's document."""
+    earlier blocks that overlap the query's document.  With ``coherent`` the
+    picks are drawn once per (index head, query block, document) and shared by
+    its queries (a labelled extra, not the per-query workload)."""
+    if coherent:
+        return _block_table_coherent(g, doc_lens, Hidx, block_size, n_random)
     T = int(np.sum(doc_lens))
     NB = -(-T // block_size)
     cu = _cu(doc_lens)
@@ -171,17 +175,35 @@ def _block_table(g, doc_lens, Hidx: int, block_size: int, n_random: int) -> np.n
     return table
 
 
+def _block_table_coherent(g, doc_lens, Hidx: int, block_size: int, n_random: int) -> np.ndarray:
+    T = int(np.sum(doc_lens))
+    NB = -(-T // block_size)
+    cu = _cu(doc_lens)
+    table = np.zeros((1, Hidx, T, NB), dtype=np.uint8)
+    for hi in range(Hidx):
+        for d in range(len(doc_lens)):
+            s0, s1 = int(cu[d]), int(cu[d + 1])
+            lo = s0 // block_size
+            for qb in range(s0 // block_size, (s1 - 1) // block_size + 1):
+                r0, r1 = max(s0, qb * block_size), min(s1, (qb + 1) * block_size)
+                cand = np.arange(lo, qb)
+                pick = g.permutation(cand)[:min(n_random, len(cand))]
+                table[0, hi, r0:r1, pick] = 1
+                table[0, hi, r0:r1, qb] = 1
+    return table
+
+
 def blocksel_case(doc_lens, Hq: int, Hkv: int, D: int, *, block_size: int = 64, n_random: int = 15,
                   Hidx: int | None = None, dtype: str = "bf16", sink_mode: str = "none",
                   sink_range=(-2.0, 2.0), seed: int = 0, scale: float | None = None,
-                  name: str = "blocksel") -> dict:
+                  coherent: bool = False, name: str = "blocksel") -> dict:
     g = rng(seed)
     T = int(np.sum(doc_lens))
     Hidx = Hkv if Hidx is None else Hidx
     q = _values(g, (T, Hq, D), 1.0, dtype)
     k = _values(g, (T, Hkv, D), 1.0, dtype)
     v = _values(g, (T, Hkv, D), 1.0, dtype)
-    table = _block_table(g, doc_lens, Hidx, block_size, n_random)
+    table = _block_table(g, doc_lens, Hidx, block_size, n_random, coherent=coherent)
     return dict(name=name, dtype=dtype, q=q, k=k, v=v, v_aliases_k=False, mask_kind="blocksel",
                 cu_seqlens=_cu(doc_lens), window=None, topk_idx=None, block_sel=table,
                 block_size=int(block_size), sinks=_sinks(g, Hq, sink_mode, sink_range),
@@ -279,6 +301,12 @@ WORKLOADS = {
     "blocksparse_32k": lambda seed=0, sink_mode="none": blocksel_case(
         c5_doc_lens(seed), 32, 8, 128, block_size=64, n_random=15, sink_mode=sink_mode,
         sink_range=(-2.0, 2.0), seed=seed, name="blocksparse_32k"),
+    # Labelled extra: the same layer with the 15 earlier blocks drawn once per
+    # 64-query block (shared by its queries), as a selection that neighbouring
+    # queries agree on would look; not the per-query workload above.
+    "blocksparse_32k_coherent": lambda seed=0, sink_mode="none": blocksel_case(
+        c5_doc_lens(seed), 32, 8, 128, block_size=64, n_random=15, sink_mode=sink_mode,
+        sink_range=(-2.0, 2.0), seed=seed, coherent=True, name="blocksparse_32k_coherent"),
 }
 
 
