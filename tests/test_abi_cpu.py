@@ -322,3 +322,24 @@ def test_decode_validation(sam):
     assert sam.STATUS[decode_check(sam, decode_args(), ws_bytes=64)] == "ATTN_ERR_RANGE"
     b = decode_args(Hq=32)
     assert sam.STATUS[decode_check(sam, b)] == "ATTN_ERR_UNSUPPORTED"
+
+
+def test_empty_inputs_return_without_launching(sam):
+    """T == 0 (or n == 0) is a valid call that enqueues nothing: every entry
+    point returns ATTN_OK on a host without a GPU, because it never reaches a
+    launch."""
+    a = merge_args(T=0)
+    assert sam.attn_sink_merge_check(a["parts"], a["sinks"], a["sink_mode"], a["out"], a["lse"]) == 0
+    sam.attn_sink_merge(a["parts"], a["sinks"], a["sink_mode"], a["out"], a["lse"], stream=0)
+    k = key0_args(T=0)
+    k["cu_seqlens"] = torch.tensor([0], dtype=torch.int32)
+    k["num_seqs"] = 0
+    sam.attn_sink_key0_correct(k["q"], k["k"], k["v"], k["cu_seqlens"], k["window"], k["sinks"], k["scale"],
+                               k["out"], k["lse"], stream=0)
+    empty = torch.empty(0, 8, dtype=torch.float32)
+    sam.attn_sink_cp_permute_rows(empty, torch.empty(0, dtype=torch.int64), True, torch.empty(0, 8), stream=0)
+    sam.attn_sink_cp_slots(3, 0, -1, torch.empty(0, dtype=torch.int64), stream=0)
+    d = decode_args(T=0)
+    ws = torch.empty(16, dtype=torch.uint8)
+    sam.attn_sink_mla_decode_fp8(d["q"], d["kv"], d["kv_scale"], d["topk_idx"], d["sinks"], d["sink_mode"], d["scale"],
+                                 d["out"], d["lse"], ws, stream=0)
