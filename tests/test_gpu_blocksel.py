@@ -106,6 +106,23 @@ def test_blocksel_table_offsets_past_2_31():
     assert math.isfinite(rel)
 
 
+def test_blocksel_document_past_one_selection_window():
+    """A 70,000-token document spans 1094 key blocks, more than the 1024
+    blocks of selection bits the kernel holds per pass, so its late rows are
+    computed over several passes whose online-softmax state carries over.
+    The sampled rows include rows that picked blocks on both sides of block
+    1024 (NeMo "cp_sparse_attn" page: per-query selection over all earlier
+    causal blocks of the document)."""
+    case = W.blocksel_case([70000, 300], 4, 1, 128, n_random=15, Hidx=1, sink_mode="null_logit",
+                           sink_range=(-2, 2), seed=15)
+    tab = case["block_sel"][0, 0]
+    late = np.arange(1024 * 64 + 64, 70000, 7)
+    straddle = [int(i) for i in late if tab[i, :1024].any() and tab[i, 1024:].sum() > 1]
+    assert len(straddle) >= 20
+    rows = G.sample_rows(case, 24, seed=6, extra=straddle[:24])
+    G.assert_parity(case, rows=rows, label="blocksel 70000-token document")
+
+
 def test_blocksel_f32_instance():
     case = W.blocksel_case([90, 41], 4, 2, 32, block_size=16, n_random=3, Hidx=1, dtype="f32",
                            sink_mode="key0_bias", sink_range=(-2, 2), seed=14)

@@ -108,3 +108,30 @@ def test_topk_f32_instance():
     G.assert_parity(case, label="f32 topk GQA")
     mla32 = W.topk_case(12, 300, 64, 576, 512, 50, counts=(1, 9, 50), dtype="f32", seed=7)
     G.assert_parity(mla32, label="f32 topk MLA")
+
+
+def test_mla_latent_rows_past_2_31():
+    """The shared latent KV is a strided view with a 4 MB row stride, so every
+    entry from row 1024 on starts 2**31 elements (4 GiB) or more into the
+    allocation; the gathers are correct only with 64-bit row offsets.  The top-k lists favour
+    those high rows (DeepSeek-V4 sparse-MLA page: indices address one shared
+    latent cache)."""
+    import torch
+    case = W.topk_case(24, 3000, 64, 576, 512, 256, counts=(1, 17, 256), shuffled=True, seed=8)
+    idx = case["topk_idx"]
+    g = np.random.default_rng(8)
+    for i in range(idx.shape[0]):                     # distinct rows >= 1024 in the same slots
+        slots = np.flatnonzero(idx[i] >= 0)
+        idx[i, slots] = g.choice(np.arange(1024, 3000), size=len(slots), replace=False)
+    stride = 1 << 21                                  # elements: 4 MB per latent row
+    assert 1024 * stride >= 2 ** 31
+    big = torch.zeros(3000 * stride, dtype=torch.bfloat16, device="cuda:0")
+    kv = big.as_strided((3000, 1, 576), (stride, 576, 1))
+    kv.copy_(torch.from_numpy(case["k"]).to(torch.bfloat16))
+    out, lse = G.gpu_run(case, k=kv, v=kv[:, :, :512])
+    ref_o, ref_l = G.oracle_run(case)
+    rel, dl = G.compare(out, lse, ref_o, ref_l)
+    G.say(f"[mla >2^31 row offsets] rel {rel:.3e} lse {dl:.3e}")
+    assert rel <= G.BF16_REL_L2 and dl <= G.BF16_LSE_ABS
+    del big, kv
+    torch.cuda.empty_cache()
