@@ -52,9 +52,6 @@ struct Params {
 __device__ __forceinline__ floatx4 mfma32(bf16x8 a, bf16x8 b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
-__device__ __forceinline__ floatx4 mfma16(bf16x4 a, bf16x4 b, floatx4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
-}
 
 // Transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group, lane
 // j reads 4 consecutive 16-bit values at its own address; the group's 16 x 4
