@@ -489,7 +489,7 @@ def main(argv=None):
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): this build has no multi-GPU path; "
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the library has no multi-GPU path (each GPU runs the same kernels on its own share); "
               "run with --gpus 1", file=sys.stderr)
         return 2
     import torch
