@@ -143,9 +143,11 @@ def load_traffic(workload: str, kind: str):
 
 
 # ----------------------------------------------------------------- workloads
-def build_case(name: str, seed: int, sink_mode: str | None):
+def build_case(name: str, seed: int, sink_mode: str | None, gqa: bool = False):
     import workloads as W
     kw = {} if sink_mode is None else {"sink_mode": sink_mode}
+    if gqa:
+        kw["gqa"] = True
     return W.make_workload(name, seed=seed, **kw)
 
 
@@ -472,6 +474,7 @@ def main(argv=None):
                              "mla_decode_fp8"])
     ap.add_argument("--sink-mode", default=None, choices=[None, "none", "key0_bias", "null_logit"])
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--gqa", action="store_true", help="window_4k: the GQA variant (16 query heads over 4 kv heads)")
     ap.add_argument("--sets", type=int, default=0, help="input sets to rotate (0: enough to exceed the MALL)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle sample budget (0: skip)")
     ap.add_argument("--compare-sink-none", action="store_true",
@@ -501,8 +504,12 @@ def main(argv=None):
         import __graft_entry__
         __graft_entry__.build()
 
-    log(f"[bench] building workload {args.workload} seed {args.seed}")
-    case = build_case(args.workload, args.seed, args.sink_mode)
+    if args.gqa and args.workload != "window_4k":
+        print("--gqa applies to the window_4k workload only", file=sys.stderr)
+        return 2
+    workload = args.workload + ("_gqa" if args.gqa else "")
+    log(f"[bench] building workload {workload} seed {args.seed}")
+    case = build_case(args.workload, args.seed, args.sink_mode, args.gqa)
     if case["mask_kind"] == "topk_fp8":
         return bench_decode(args, case)
     prow = pairs_per_row(case)
@@ -532,17 +539,17 @@ def main(argv=None):
         ach = F / (kern_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": ach, "peak": PEAK_MFMA_BF16_TFS, "unit": "TFLOP/s",
                 "frac": ach / PEAK_MFMA_BF16_TFS}
-    roof["traffic"] = load_traffic(args.workload + ":" + case["sink_mode"], kind)
+    roof["traffic"] = load_traffic(workload + ":" + case["sink_mode"], kind)
     roof["kernel_ms"] = kern_ms
     roof["algorithmic_bytes"] = B
     roof["useful_flops"] = F
 
     value = F / (ms * 1e-3) / 1e12
-    page = PAGE_MS.get((args.workload, case["sink_mode"]))
+    page = PAGE_MS.get((workload, case["sink_mode"]))
     res = {"metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
            "vs_baseline": (page / ms) if page else None, "dtype": case["dtype"], "data": "synthetic",
-           "config": describe(args.workload, case, sets_n), "roofline": roof}
+           "config": describe(workload, case, sets_n), "roofline": roof}
 
     if args.compare_sink_none and case["sink_mode"] != "none":
         base = dict(case, sink_mode="none", sinks=None)
