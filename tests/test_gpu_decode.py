@@ -69,3 +69,33 @@ def test_decode_neg_inf_sink_is_bitwise_noop():
     assert torch.equal(b["out"], none["out"]) and torch.equal(b["lse"], none["lse"])
     assert torch.equal(a["lse"], none["lse"])          # the LSE never includes the sink
     assert not torch.equal(a["out"], none["out"])
+
+
+def test_decode_cache_rows_past_2_31():
+    """The fp8 cache is a strided view with a row stride just over 2 MB, so
+    every entry from row 1024 on starts past byte 2**31 of the allocation (an
+    fp8 element is a byte): the gathers are correct only with 64-bit row
+    offsets.  The lists address only those rows (distinct per row)."""
+    case = W.mla_decode_fp8_case(24, 3000, 64, 256, counts=(1, 17, 256), shuffled=True, seed=8)
+    idx = case["topk_idx"]
+    g = np.random.default_rng(8)
+    for i in range(idx.shape[0]):
+        slots = np.flatnonzero(idx[i] >= 0)
+        idx[i, slots] = g.choice(np.arange(1024, 3000), size=len(slots), replace=False)
+    stride = (1 << 21) + 4096                          # bytes per cache row
+    assert 1024 * stride > 2 ** 31
+    d = G.sam().decode_case_on_device(case)
+    big = torch.zeros(3000 * stride, dtype=torch.uint8, device="cuda:0")
+    kv = big.as_strided((3000, 1, 576), (stride, 576, 1))
+    kv.copy_(torch.from_numpy(case["kv_fp8"]).cuda())
+    G.sam().attn_sink_mla_decode_fp8(d["q"], kv.view(torch.float8_e4m3fn), d["kv_scale"], d["topk_idx"],
+                                     d["sinks"], d["sink_mode"], d["scale"], d["out"], d["lse"], d["workspace"])
+    torch.cuda.synchronize()
+    out = d["out"].float().cpu().numpy().astype(np.float64)
+    lse = d["lse"].cpu().numpy().astype(np.float64)
+    ref_o, ref_l = fp8.decode_ref(case)
+    rel, dl = G.compare(out, lse, ref_o, ref_l)
+    G.say(f"[decode >2^31 row offsets] rel {rel:.3e} lse {dl:.3e}")
+    assert rel <= G.BF16_REL_L2 and dl <= G.BF16_LSE_ABS
+    del big, kv
+    torch.cuda.empty_cache()
