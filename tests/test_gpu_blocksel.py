@@ -127,3 +127,30 @@ def test_blocksel_f32_instance():
     case = W.blocksel_case([90, 41], 4, 2, 32, block_size=16, n_random=3, Hidx=1, dtype="f32",
                            sink_mode="key0_bias", sink_range=(-2, 2), seed=14)
     G.assert_parity(case, label="f32 blocksel")
+
+
+def test_blocksel_kv_rows_past_2_31():
+    """K and V are strided views with a 16 MB token stride, so every key
+    block from token 128 on starts past byte 2**31 of its allocation: the
+    block loads are correct only with a 64-bit block base."""
+    import torch
+    case = W.blocksel_case([200, 190], 8, 2, 128, n_random=3, Hidx=2, sink_mode="null_logit", seed=16)
+    T, Hkv, D = case["k"].shape
+    stride = (1 << 23) + 64
+    assert 128 * stride * 2 > 2 ** 31
+
+    def strided(a):
+        big = torch.zeros(T * stride, dtype=torch.bfloat16, device="cuda:0")
+        view = big.as_strided((T, Hkv, D), (stride, D, 1))
+        view.copy_(torch.from_numpy(a).to(torch.bfloat16))
+        return big, view
+
+    kb, k = strided(case["k"])
+    vb, v = strided(case["v"])
+    out, lse = G.gpu_run(case, k=k, v=v)
+    ref_o, ref_l = G.oracle_run(case)
+    rel, dl = G.compare(out, lse, ref_o, ref_l)
+    G.say(f"[blocksel >2^31 row offsets] rel {rel:.3e} lse {dl:.3e}")
+    assert rel <= G.BF16_REL_L2 and dl <= G.BF16_LSE_ABS
+    del kb, vb, k, v
+    torch.cuda.empty_cache()

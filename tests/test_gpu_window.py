@@ -127,3 +127,31 @@ def test_membership_probe():
         i = np.arange(T)
         want = (seg == seg[j]) & (np.abs(i - j) <= Wd)
         assert np.array_equal(got, np.repeat(want[:, None], 2, axis=1)), j
+
+
+def test_window_kv_rows_past_2_31():
+    """K and V are strided views with a 16 MB token stride, so every key row
+    from token 128 on starts past byte 2**31 of its allocation: the band loads
+    are correct only with 64-bit row offsets."""
+    import torch
+    case = W.window_case([120, 180], 4, 2, 80, 16, dtype="bf16", sink_mode="key0_bias", sink_range=(-2, 2),
+                         seed=21)
+    T, Hkv, D = case["k"].shape
+    stride = (1 << 23) + 64                            # elements per token row
+    assert 128 * stride * 2 > 2 ** 31
+
+    def strided(a):
+        big = torch.zeros(T * stride, dtype=torch.bfloat16, device="cuda:0")
+        view = big.as_strided((T, Hkv, D), (stride, D, 1))
+        view.copy_(torch.from_numpy(a).to(torch.bfloat16))
+        return big, view
+
+    kb, k = strided(case["k"])
+    vb, v = strided(case["v"])
+    out, lse = G.gpu_run(case, k=k, v=v)
+    ref_o, ref_l = G.oracle_run(case)
+    rel, dl = G.compare(out, lse, ref_o, ref_l)
+    G.say(f"[window >2^31 row offsets] rel {rel:.3e} lse {dl:.3e}")
+    assert rel <= G.BF16_REL_L2 and dl <= G.BF16_LSE_ABS
+    del kb, vb, k, v
+    torch.cuda.empty_cache()
