@@ -38,7 +38,10 @@
  *     live in host memory and are read during the call only.
  *   - Strides are in elements.  The innermost dimension of q, k, v and out must
  *     be contiguous (stride 1); the other strides are free but must keep every
- *     row 16-byte aligned (bf16: multiples of 8 elements; f32: of 4).
+ *     row 16-byte aligned (bf16: multiples of 8 elements; f32: of 4), and 64
+ *     rows must span less than 2^31 bytes (kernels address inside a 64-row
+ *     tile with 32-bit offsets from a 64-bit tile base; ATTN_ERR_RANGE
+ *     otherwise).  Offsets across the whole tensor are 64-bit.
  *   - The caller owns every buffer, including the one scratch buffer (the fp8
  *     decode's workspace).  The library allocates nothing and keeps no
  *     mutable global state: calls are reentrant and may run concurrently on
@@ -112,7 +115,7 @@ typedef enum attn_status {
   ATTN_ERR_HEADS = -5,       /* Hq % Hkv != 0, or Hq % Hidx != 0                 */
   ATTN_ERR_DTYPE = -6,       /* dtypes disagree or are not allowed for a role    */
   ATTN_ERR_UNSUPPORTED = -7, /* well-formed, but no kernel instance covers it    */
-  ATTN_ERR_RANGE = -8,       /* a size or value is out of range (T >= 2^31, W<0) */
+  ATTN_ERR_RANGE = -8,       /* a size, stride or value is out of range (T >= 2^31, W < 0, 64 rows >= 2^31 bytes) */
   ATTN_ERR_LAUNCH = -9       /* the kernel launch itself failed                  */
 } attn_status;
 

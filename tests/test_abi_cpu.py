@@ -343,3 +343,20 @@ def test_empty_inputs_return_without_launching(sam):
     ws = torch.empty(16, dtype=torch.uint8)
     sam.attn_sink_mla_decode_fp8(d["q"], d["kv"], d["kv_scale"], d["topk_idx"], d["sinks"], d["sink_mode"], d["scale"],
                                  d["out"], d["lse"], ws, stream=0)
+
+
+def test_row_stride_limit_of_a_64_row_tile(sam):
+    """64 rows of q, k, v or out must span less than 2^31 bytes (kernels
+    address inside a 64-row tile with 32-bit offsets): a bf16 row stride of
+    2^24 elements is refused with ATTN_ERR_RANGE, one 64 elements shorter is
+    accepted.  Single-row tensors carry the stride without any storage."""
+    base = window_args(T=1, Hq=4, Hkv=4, D=64)
+    base.update(cu_seqlens=torch.tensor([0, 1], dtype=torch.int32), num_seqs=1)
+
+    def strided(t, s0):
+        return t.as_strided(t.shape, (s0,) + tuple(t.stride()[1:]))
+
+    for key in ("q", "k", "v", "out"):
+        ok = dict(base, **{key: strided(base[key], (1 << 24) - 64)})
+        assert check(sam, ok) == 0, key
+        _bad(sam, base, "ATTN_ERR_RANGE", **{key: strided(base[key], 1 << 24)})
