@@ -168,7 +168,7 @@ void blocksel_fwd_bf16(const Params p) {
     }
   };
 
-  // ---- one staged block for this wave's 4 column blocks
+  // ---- one staged block for this wave's column blocks
   auto compute = [&](int blk, int wsel, const bf16* st) {
     const int kb0 = blk * BS;
     const bf16* ks = st;
