@@ -428,9 +428,8 @@ def bench_decode(args, case):
                       "sink_mode": case["sink_mode"], "cold_cache_sets": sets_n},
            "roofline": {"bound": "mfma", "achieved": ach, "peak": PEAK_MFMA_BF16_TFS, "unit": "TFLOP/s",
                         "frac": ach / PEAK_MFMA_BF16_TFS, "traffic": None, "kernel_ms": kern_ms,
-                        "algorithmic_bytes": B, "useful_flops": F,
-                        "hbm_GBps": B / (kern_ms * 1e-3) / 1e9},
-           "wall_s": time.perf_counter() - t0}
+                        "algorithmic_bytes": B, "useful_flops": F, **both_roofs(F, B, kern_ms)},
+           "device": device_facts(), "wall_s": time.perf_counter() - t0}
     d = sets[0]
     sam.attn_sink_mla_decode_fp8(d["q"], d["kv"], d["kv_scale"], d["topk_idx"], d["sinks"], d["sink_mode"],
                                  d["scale"], d["out"], d["lse"], d["workspace"])
@@ -462,6 +461,49 @@ def bench_decode(args, case):
         res["cpu_baseline"] = None
     print(json.dumps(res), flush=True)
     return 0
+
+
+def both_roofs(F: float, B: float, kern_ms: float) -> dict:
+    """The launch against both roofs: useful FLOP/s against the MFMA peak and
+    algorithmic bytes/s against the HBM peak (the binding one is `frac`)."""
+    t = kern_ms * 1e-3
+    return {"hbm_GBps": B / t / 1e9, "hbm_frac": B / t / 1e9 / PEAK_HBM_GBS,
+            "mfma_TFLOPs": F / t / 1e12, "mfma_frac": F / t / 1e12 / PEAK_MFMA_BF16_TFS}
+
+
+def device_facts(copy_bytes: int = 1 << 30, reps: int = 10) -> dict:
+    """What the box reports (name, compute units, architecture) and the HBM
+    bandwidth two plain copies of copy_bytes reach here (bytes read + written
+    per second): torch's device copy, and the library's row gather
+    (attn_sink_cp_permute_rows) with the identity index over 64 KB rows."""
+    import torch
+    import sink_aware_masked_amd as sam
+    props = torch.cuda.get_device_properties(0)
+    a = torch.empty(copy_bytes, dtype=torch.uint8, device="cuda:0").fill_(1)
+    b = torch.empty_like(a)
+    rows = copy_bytes // 65536
+    a2, b2 = a.view(rows, 65536), b.view(rows, 65536)
+    ident = torch.arange(rows, dtype=torch.int64, device="cuda:0")
+
+    def rate(fn):
+        for _ in range(2):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return 2 * copy_bytes / (e0.elapsed_time(e1) / reps * 1e-3) / 1e9
+
+    torch_gbs = rate(lambda: b.copy_(a))
+    rows_gbs = rate(lambda: sam.attn_sink_cp_permute_rows(a2, ident, False, b2))
+    assert torch.equal(a, b)
+    del a, b, a2, b2, ident
+    torch.cuda.empty_cache()
+    return {"name": props.name, "compute_units": props.multi_processor_count,
+            "arch": getattr(props, "gcnArchName", None), "copy_bytes": 2 * copy_bytes,
+            "copy_GBps_torch": torch_gbs, "copy_GBps_row_gather": rows_gbs}
 
 
 def main(argv=None):
@@ -540,6 +582,7 @@ def main(argv=None):
         roof = {"bound": "mfma", "achieved": ach, "peak": PEAK_MFMA_BF16_TFS, "unit": "TFLOP/s",
                 "frac": ach / PEAK_MFMA_BF16_TFS}
     roof["traffic"] = load_traffic(workload + ":" + case["sink_mode"], kind)
+    roof.update(both_roofs(F, B, kern_ms))
     roof["kernel_ms"] = kern_ms
     roof["algorithmic_bytes"] = B
     roof["useful_flops"] = F
@@ -549,7 +592,7 @@ def main(argv=None):
     res = {"metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
            "vs_baseline": (page / ms) if page else None, "dtype": case["dtype"], "data": "synthetic",
-           "config": describe(workload, case, sets_n), "roofline": roof}
+           "config": describe(workload, case, sets_n), "roofline": roof, "device": device_facts()}
 
     if args.compare_sink_none and case["sink_mode"] != "none":
         base = dict(case, sink_mode="none", sinks=None)
