@@ -68,3 +68,9 @@ def test_blocksparse_32k_pairs_on_sampled_rows():
     for i in g.choice(case["q"].shape[0], size=40, replace=False):
         want = sum(P.closed_form_count(case, int(i), h) for h in range(32))
         assert got[i] == want, int(i)
+
+
+def test_bench_refuses_more_than_one_gpu(capsys):
+    """One GPU only: --gpus above 1 exits with status 2 and says why."""
+    assert bench.main(["--gpus", "2"]) == 2
+    assert "one GPU only" in capsys.readouterr().err
