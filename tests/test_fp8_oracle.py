@@ -48,3 +48,51 @@ def test_decode_matches_topk_oracle_on_dequantized_cache():
     o3, _ = oracle.attn_ref(case["q"], kb, kb[:, :, :512], mask_kind="topk", scale=case["scale"],
                             topk_idx=case["topk_idx"], sinks=case["sinks"], sink_mode="null_logit")
     assert not np.allclose(o1, o3, rtol=1e-3, atol=1e-6)
+
+
+def _golden_dequant():
+    import json
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", "fp8_dequant.json")
+    return json.load(open(path))["cases"]
+
+
+def _check_fixtures(dequantize_fn) -> bool:
+    """True iff dequantize_fn reproduces every hand-worked (byte, row scale)
+    value, sign of zero included."""
+    for c in _golden_dequant():
+        b = np.array([[[int(c["byte"], 16)]]], dtype=np.uint8)
+        got = float(dequantize_fn(b, np.array([c["scale"]], dtype=np.float32))[0, 0, 0])
+        if got != c["value"] or math.copysign(1, got) != math.copysign(1, c["value"]):
+            return False
+    return True
+
+
+def test_dequantize_hand_worked_fixtures():
+    """Per-row scaling pinned to values worked by hand (tests/golden/fp8_dequant.json):
+    value = e4m3(byte) * scale[row].  Plausible wrong conventions fail it."""
+    assert _check_fixtures(fp8.dequantize)
+    divide = lambda b, s: fp8.e4m3_to_float(b) / np.asarray(s, dtype=np.float64)[:, None, None]
+    assert not _check_fixtures(divide), "dividing by the row scale must fail the fixtures"
+    forget = lambda b, s: fp8.e4m3_to_float(b) + 0.0 * np.asarray(s, dtype=np.float64)[:, None, None]
+    assert not _check_fixtures(forget), "ignoring the row scale must fail the fixtures"
+
+
+def test_dequantize_within_half_ulp_of_source_rows():
+    """The generator rounds fp32 rows x to e4m3 after dividing by the row scale
+    (round to nearest even); dequantizing must land within half an e4m3 unit in
+    the last place of x / scale, times the scale, of x.  A divide-by-scale or a
+    transposed scale (wrong row) lands far outside it."""
+    case = W.mla_decode_fp8_case(2, 512, 64, 16, counts=(16,), seed=5)
+    x = case["kv_source"].astype(np.float64)                    # [Tk, 576]
+    sc = case["kv_scale"].astype(np.float64)[:, None]
+    y = np.abs(x / sc)
+    assert y.max() <= 448.0
+    e = np.floor(np.log2(np.maximum(y, 2.0 ** -6)))             # exponent; subnormal range has e = -6
+    half_ulp = 0.5 * np.exp2(e - 3) * sc                          # 3 mantissa bits
+    err = np.abs(fp8.dequantize(case["kv_fp8"], case["kv_scale"])[:, 0, :] - x)
+    assert np.all(err <= half_ulp * (1 + 1e-12)), float((err / half_ulp).max())
+    wrong = fp8.e4m3_to_float(case["kv_fp8"])[:, 0, :] / sc
+    assert not np.all(np.abs(wrong - x) <= half_ulp)
+    shifted = fp8.e4m3_to_float(case["kv_fp8"])[:, 0, :] * np.roll(sc, 1, axis=0)
+    assert not np.all(np.abs(shifted - x) <= half_ulp)

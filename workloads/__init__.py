@@ -217,7 +217,8 @@ def mla_decode_fp8_case(T: int, Tk: int, Hq: int, topk: int, *, counts=(2048,), 
     cache rows drawn N(0, std^2) in fp32, each stored as 576 fp8 e4m3 bytes
     (round to nearest even, by torch's float8_e4m3fn conversion) with one fp32
     scale per row, amax / 448 rounded up to an 8-bit mantissa (so scale times
-    any e4m3 value is exact in fp32).  Top-k lists as in topk_case."""
+    any e4m3 value is exact in fp32).  Top-k lists as in topk_case.  The fp32
+    rows before rounding are kept as ``kv_source`` [Tk, 576]."""
     import torch
     base = topk_case(T, Tk, Hq, 576, 512, topk, counts=counts, shuffled=shuffled, mla=True, std=std,
                      sink_mode=sink_mode, sink_range=sink_range, seed=seed, out_of_range=out_of_range, name=name)
@@ -230,7 +231,7 @@ def mla_decode_fp8_case(T: int, Tk: int, Hq: int, topk: int, *, counts=(2048,), 
     sc = ((bits & np.uint32(0xFFFF0000)) + (up.astype(np.uint32) << np.uint32(16))).view(np.float32)  # round up
     q8 = torch.from_numpy(x / sc[:, None]).to(torch.float8_e4m3fn)
     fp8 = q8.view(torch.uint8).numpy().reshape(Tk, 1, 576).copy()
-    base.update(kv_fp8=fp8, kv_scale=sc.astype(np.float32), k=None, v=None, v_aliases_k=True,
+    base.update(kv_fp8=fp8, kv_scale=sc.astype(np.float32), kv_source=x, k=None, v=None, v_aliases_k=True,
                 mask_kind="topk_fp8")
     return base
 
