@@ -13,10 +13,11 @@ over that augmented row then gives the output; the LSE is taken over the
 selected keys only.  Sources:
 
 * ``key0_bias`` -- "[Bugfix][MiMo] Apply vision attention sinks in the window
-  attention path": sinks[h] is added to the logit of each sequence's first key
-  (after scaling: the page's closed form multiplies key 0's weight by exp(s)).
+  attention path", closed-form correction paragraph: a per-head bias on key 0
+  of every sequence, applied after scaling (the closed form multiplies key 0's
+  weight by exp(s)).
 * window -- same page: symmetric window inside each cu_seqlens sequence; the
-  bound is inclusive (only the first window_size + 1 queries see key 0).
+  bound is inclusive (rows 0 .. W of a sequence, W + 1 of them, reach key 0).
 * ``null_logit`` -- "Apply DeepSeek-V4 attn_sink in the XPU sparse-MLA Triton
   kernel", Implementation paragraph: the sink joins the softmax denominator,
   the returned LSE covers the selected keys only; top-k lists use -1 padding.

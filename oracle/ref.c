@@ -13,10 +13,10 @@
  *     l_j     = scale * sum_d q[i,h,d] * k[j,kv,d]                for j in S
  *     key0_bias: l_j += sinks[h] when j is the first key of its cu_seqlens
  *                segment ("[Bugfix][MiMo] Apply vision attention sinks in the
- *                window attention path": the reference adds sinks[h] to the
- *                logit of each sequence's first key; the sink is added to the
- *                already-scaled logit, as the page's closed-form correction
- *                multiplies key 0's softmax weight by exp(s)).
+ *                window attention path", closed-form correction paragraph: the
+ *                per-head sink biases key 0 of every sequence; it enters the
+ *                already-scaled logit, since that correction multiplies key
+ *                0's softmax weight by exp(s)).
  *     empty S: out = 0, lse = -inf ("cp_sparse_attn" API page,
  *              _local_sparse_forward: fully masked rows give zero output).
  *     m = max l_j, Z = sum exp(l_j - m), A = sum exp(l_j - m) * v[j,kv,:]
@@ -30,8 +30,8 @@
  *
  * Mask kinds:
  *   window   (mask_kind 0): j in the same cu_seqlens segment as i and
- *            |i - j| <= W.  The bound is inclusive: the MiMo page says only
- *            the first window_size + 1 queries of a sequence can see key 0.
+ *            |i - j| <= W.  The bound is inclusive: on the MiMo page the rows
+ *            that reach key 0 are the sequence's first W + 1 (rows 0 .. W).
  *   topk     (mask_kind 1): j = topk_idx[i, t] for every t with
  *            0 <= topk_idx[i, t] < Tk; -1 (or anything outside) is padding.
  *            The list is shared by all heads (sparse MLA with one latent KV).

@@ -142,6 +142,57 @@ def _ref(x):
     return None if x is None else ctypes.byref(x)
 
 
+def _on_device(name, t, device):
+    """Raise unless t is a torch tensor on `device` (a host pointer handed to a
+    kernel would fault the GPU)."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor on {device}, got {type(t).__name__}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _aux(name, t, dtype, numel, device, *, optional=False, at_least=False):
+    """Check a buffer the C ABI takes as a bare pointer: a contiguous torch
+    tensor on `device` with the given dtype and element count (or at least
+    that many elements), checked before anything is enqueued."""
+    import torch
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    _on_device(name, t, device)
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if (t.numel() < numel) if at_least else (t.numel() != numel):
+        raise ValueError(f"{name} has {t.numel()} elements, expected {'at least ' if at_least else ''}{numel}")
+
+
+def _check_fwd_buffers(q, k, v, out, cu_seqlens, sinks, lse, topk_idx, block_sel, sink_mode):
+    import torch
+    dev = q.device
+    for name, t in (("k", k), ("v", v), ("out", out)):
+        _on_device(name, t, dev)
+    for name, t in (("topk_idx", topk_idx), ("block_sel", block_sel)):
+        if t is not None and not isinstance(t, AttnTensor):
+            _on_device(name, t, dev)
+    T, Hq = q.shape[0], q.shape[1]
+    if cu_seqlens is not None:
+        _aux("cu_seqlens", cu_seqlens, torch.int32, max(cu_seqlens.numel(), 1), dev)
+    _aux("sinks", sinks, torch.float32, Hq, dev, optional=(sink_mode == 0))
+    _aux("lse", lse, torch.float32, Hq * T, dev)
+    _need_gpu(q)
+
+
+def _need_gpu(t):
+    """Non-empty calls launch kernels, which need device memory (an empty call
+    enqueues nothing and is accepted anywhere)."""
+    if t.numel() > 0 and t.device.type != "cuda":
+        raise ValueError(f"the kernels need device memory; got tensors on {t.device}")
+
+
 def _as_desc(x):
     if x is None or isinstance(x, AttnTensor):
         return x
@@ -186,6 +237,7 @@ def attn_sink_fwd(q, k, v, cu_seqlens, mask_kind, mask: dict, sinks, sink_mode, 
     Raises AttnSinkError on a non-zero status."""
     import torch
     mk, sm = _codes(mask_kind, sink_mode)
+    _check_fwd_buffers(q, k, v, out, cu_seqlens, sinks, lse, mask.get("topk_idx"), mask.get("block_sel"), sm)
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
     elif hasattr(stream, "cuda_stream"):
@@ -209,6 +261,7 @@ def prepared_fwd(q, k, v, *, mask_kind: str, scale: float, out, lse, cu_seqlens=
     where per-call Python marshalling would dominate a microsecond kernel)."""
     import torch
     mk, sm = _codes(mask_kind, sink_mode)
+    _check_fwd_buffers(q, k, v, out, cu_seqlens, sinks, lse, topk_idx, block_sel, sm)
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
     elif hasattr(stream, "cuda_stream"):
@@ -264,6 +317,8 @@ def attn_sink_key0_correct(q, k, v, cu_seqlens, window, sinks, scale, out, lse, 
     """Rewrite, in place, the out / lse of a no-sink window attention with the
     closed-form key-0 sink (only the first window + 1 rows of each sequence).
     Raises AttnSinkError on a non-zero status."""
+    import torch
+    _check_fwd_buffers(q, k, v, out, cu_seqlens, sinks, lse, None, None, 1)
     num_seqs = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
     dq, dk, dv, do = desc(q), desc(k), desc(v), desc(out)
     rc = _lib.attn_sink_key0_correct(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), _ptr(cu_seqlens),
@@ -295,6 +350,16 @@ def attn_sink_merge(parts, sinks, sink_mode, out, lse, stream=None) -> None:
     """Merge partial results over disjoint key sets, parts = [(out_p, lse_p), ...]
     (each from a no-sink attn_sink_fwd), into out / lse, folding in a
     null_logit sink after the merge.  Raises AttnSinkError on a non-zero status."""
+    import torch
+    dev = out.device
+    T, Hq = out.shape[0], out.shape[1]
+    sm = SINK_MODES[sink_mode] if isinstance(sink_mode, str) else int(sink_mode)
+    for i, (po, pl) in enumerate(parts):
+        _on_device(f"parts[{i}].out", po, dev)
+        _aux(f"parts[{i}].lse", pl, torch.float32, Hq * T, dev)
+    _aux("sinks", sinks, torch.float32, Hq, dev, optional=(sm != SINK_MODES["null_logit"]))
+    _aux("lse", lse, torch.float32, Hq * T, dev)
+    _need_gpu(out)
     args, keep = _merge_args(parts, sinks, sink_mode, out, lse)
     rc = _lib.attn_sink_merge(*args, ctypes.c_void_p(_stream(stream, out.device)))
     if rc != 0:
@@ -313,6 +378,10 @@ def attn_sink_cp_slots_check(cp_size, t_local, rank, slots) -> int:
 def attn_sink_cp_slots(cp_size, t_local, rank, slots, stream=None) -> None:
     """Global slot of every local slot under load-balanced causal CP (rank -1:
     all ranks, rank-major) into the int64 device tensor `slots`."""
+    import torch
+    n = int(cp_size) * int(t_local) if int(rank) < 0 else int(t_local)
+    if slots is not None:
+        _aux("slots", slots, torch.int64, n, slots.device, at_least=True)
     _check_rc(_lib.attn_sink_cp_slots(int(cp_size), int(t_local), int(rank), _ptr(slots),
                                       ctypes.c_void_p(_stream(stream, slots.device))))
 
@@ -325,6 +394,9 @@ def attn_sink_cp_permute_rows_check(src, index, n, scatter, dst) -> int:
 def attn_sink_cp_permute_rows(src, index, scatter, dst, stream=None) -> None:
     """scatter: dst[index[i]] = src[i] (order_by_positions); gather:
     dst[i] = src[index[i]] (restore_by_positions).  index: int64 device tensor."""
+    import torch
+    _on_device("dst", dst, src.device)
+    _aux("index", index, torch.int64, index.numel() if isinstance(index, torch.Tensor) else 0, src.device)
     ds, dd = desc(src), desc(dst)
     _check_rc(_lib.attn_sink_cp_permute_rows(ctypes.byref(ds), _ptr(index), int(index.numel()), int(bool(scatter)),
                                              ctypes.byref(dd), ctypes.c_void_p(_stream(stream, src.device))))
@@ -338,6 +410,13 @@ def attn_sink_cp_documents_check(positions, T, doc_ids, cu_seqlens, max_docs, nu
 def attn_sink_cp_documents(positions, doc_ids=None, cu_seqlens=None, num_docs=None, stream=None) -> None:
     """Document ids (cumsum(positions == 0) - 1) and segment boundaries of
     global-ordered int64 position ids; cu_seqlens holds max_docs + 1 entries."""
+    import torch
+    dev = positions.device
+    _aux("positions", positions, torch.int64, positions.numel(), dev)
+    _aux("doc_ids", doc_ids, torch.int32, positions.numel(), dev, optional=True)
+    _aux("num_docs", num_docs, torch.int32, 1, dev, optional=True)
+    if cu_seqlens is not None:
+        _aux("cu_seqlens", cu_seqlens, torch.int32, max(cu_seqlens.numel(), 1), dev)
     max_docs = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
     _check_rc(_lib.attn_sink_cp_documents(_ptr(positions), int(positions.numel()), _ptr(doc_ids),
                                           _ptr(cu_seqlens), int(max_docs), _ptr(num_docs),
@@ -366,6 +445,18 @@ def attn_sink_mla_decode_fp8(q, kv, kv_scale, topk_idx, sinks, sink_mode, scale,
     per-row fp32 scales; workspace: a device tensor of at least
     attn_sink_mla_decode_fp8_workspace(T, Hq, topk) bytes."""
     sm = SINK_MODES[sink_mode] if isinstance(sink_mode, str) else int(sink_mode)
+    import torch
+    dev = q.device
+    T, Hq = q.shape[0], q.shape[1]
+    for name, t in (("kv", kv), ("topk_idx", topk_idx), ("out", out)):
+        _on_device(name, t, dev)
+    _aux("kv_scale", kv_scale, torch.float32, kv.shape[0], dev)
+    _aux("sinks", sinks, torch.float32, Hq, dev, optional=(sm != SINK_MODES["null_logit"]))
+    _aux("lse", lse, torch.float32, Hq * T, dev)
+    _on_device("workspace", workspace, dev)
+    if not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    _need_gpu(q)
     dq, dk, di, do = desc(q), desc(kv), desc(topk_idx), desc(out)
     nbytes = workspace.numel() * workspace.element_size()
     _check_rc(_lib.attn_sink_mla_decode_fp8(ctypes.byref(dq), ctypes.byref(dk), _ptr(kv_scale), ctypes.byref(di),

@@ -19,6 +19,10 @@ hipError_t launch_window_bf16(const Params& p, int sink, hipStream_t st);
 hipError_t launch_generic_f32(const Params& p, int mask, int sink, hipStream_t st);
 hipError_t launch_topk_mla_bf16(const Params& p, int sink, hipStream_t st);
 hipError_t launch_blocksel_bf16(const Params& p, int sink, hipStream_t st);
+int64_t window_bf16_items(const Params& p);
+int64_t generic_f32_items(const Params& p);
+int64_t topk_mla_bf16_items(const Params& p);
+int64_t blocksel_bf16_items(const Params& p);
 }  // namespace attn
 
 static_assert(attn::kMergeMaxParts == ATTN_SINK_MERGE_MAX_PARTS, "merge part limit");
@@ -30,6 +34,9 @@ using attn::Params;
 enum Instance { kInstNone = 0, kInstGenericF32, kInstWindowBf16, kInstTopkMlaBf16, kInstBlockselBf16 };
 
 constexpr int64_t kMaxTokens = 0x7fffffffLL;
+// A launch's x dimension holds at most 2^32 - 1 work items (workgroups times
+// workgroup size); calls whose grid would exceed it are refused up front.
+constexpr int64_t kMaxGridItems = 0xffffffffLL;
 
 int elem_size(int32_t dt) {
   switch (dt) {
@@ -130,7 +137,9 @@ int prepare(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
   }
   if (mask_kind == ATTN_MASK_WINDOW) {
     if (mask->window < 0) return ATTN_ERR_RANGE;
-    P->window = mask->window;
+    // a window of T or more keys covers every sequence whole: clamp, so that
+    // no row +- window sum can leave the int32 range
+    P->window = (int)(mask->window < T ? mask->window : T);
   } else if (mask_kind == ATTN_MASK_TOPK) {
     const attn_tensor* ti = mask->topk_idx;
     if ((rc = check_tensor(ti, 2))) return rc;
@@ -159,26 +168,31 @@ int prepare(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
     P->block_size = mask->block_size;
   }
 
-  // kernel instance
+  // kernel instance, then its grid against the launch limit
+  int64_t items = 0;
   if (dt == ATTN_DTYPE_F32) {
     if (Dqk > 576 || Dv > 576) return ATTN_ERR_UNSUPPORTED;
     *inst = kInstGenericF32;
-    return ATTN_OK;
-  }
-  if (mask_kind == ATTN_MASK_WINDOW) {
+    items = attn::generic_f32_items(*P);
+  } else if (mask_kind == ATTN_MASK_WINDOW) {
     if (Dqk != Dv || !(Dqk == 64 || Dqk == 80 || Dqk == 96 || Dqk == 128)) return ATTN_ERR_UNSUPPORTED;
     *inst = kInstWindowBf16;
-    return ATTN_OK;
-  }
-  if (mask_kind == ATTN_MASK_TOPK) {
+    items = attn::window_bf16_items(*P);
+  } else if (mask_kind == ATTN_MASK_TOPK) {
     const bool shared_latent = v->data == k->data && v->stride[0] == k->stride[0] && Hkv == 1;
     if (!shared_latent || Dqk != 576 || Dv != 512 || Hq % 64 != 0) return ATTN_ERR_UNSUPPORTED;
     *inst = kInstTopkMlaBf16;
-    return ATTN_OK;
+    items = attn::topk_mla_bf16_items(*P);
+  } else {
+    if (Dqk != 128 || Dv != 128 || Hq / Hkv != 4 || mask->block_size != 64 || Hkv % P->Hidx != 0)
+      return ATTN_ERR_UNSUPPORTED;
+    *inst = kInstBlockselBf16;
+    items = attn::blocksel_bf16_items(*P);
   }
-  if (Dqk != 128 || Dv != 128 || Hq / Hkv != 4 || mask->block_size != 64 || Hkv % P->Hidx != 0)
-    return ATTN_ERR_UNSUPPORTED;
-  *inst = kInstBlockselBf16;
+  if (items > kMaxGridItems) {
+    *inst = kInstNone;
+    return ATTN_ERR_RANGE;
+  }
   return ATTN_OK;
 }
 
@@ -248,7 +262,9 @@ int prepare_key0(const attn_tensor* q, const attn_tensor* k, const attn_tensor* 
   if (!sinks) return ATTN_ERR_NULL;
   if (T > 0 && (!cu_seqlens || num_seqs < 1)) return cu_seqlens ? ATTN_ERR_RANGE : ATTN_ERR_NULL;
   if (window < 0) return ATTN_ERR_RANGE;
-  if ((int64_t)num_seqs * ((int64_t)window + 1) > kMaxTokens) return ATTN_ERR_RANGE;
+  if (window > T) window = (int32_t)T;  // rows past T do not exist: same affected rows
+  // one 256-lane workgroup per (row slot, group of 4 heads)
+  if ((int64_t)num_seqs * ((int64_t)window + 1) * 256 > kMaxGridItems) return ATTN_ERR_RANGE;
   if (!(scale == scale) || scale == __builtin_huge_valf() || scale == -__builtin_huge_valf())
     return ATTN_ERR_RANGE;
   memset(P, 0, sizeof(*P));
@@ -530,6 +546,7 @@ int prepare_decode(const attn_tensor* q, const attn_tensor* kv, const float* kv_
   if (!lse && T > 0) return ATTN_ERR_NULL;
   if (reinterpret_cast<uintptr_t>(lse) % 4 != 0) return ATTN_ERR_STRIDE;
   if (!(scale == scale) || scale == __builtin_huge_valf() || scale == -__builtin_huge_valf()) return ATTN_ERR_RANGE;
+  if (T * (Hq / 64) * 256 > kMaxGridItems) return ATTN_ERR_RANGE;  // one 256-lane workgroup per (row, 64 heads, piece)
   const int nsplit = attn::decode_splits(T, Hq, ti->shape[1]);
   if (T > 0 && (!ws || ws_bytes < decode_ws_bytes(T, Hq, nsplit))) return ws ? ATTN_ERR_RANGE : ATTN_ERR_NULL;
   if (reinterpret_cast<uintptr_t>(ws) % 16 != 0) return ATTN_ERR_STRIDE;

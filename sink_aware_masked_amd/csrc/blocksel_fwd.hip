@@ -398,6 +398,10 @@ void blocksel_fwd_bf16(const Params p) {
   }
 }
 
+int64_t blocksel_bf16_items(const Params& p) {
+  return ((int64_t)p.T + bsel::BS - 1) / bsel::BS * p.Hkv * 64 * bsel::NW;
+}
+
 hipError_t launch_blocksel_bf16(const Params& p, int sink, hipStream_t st) {
   using namespace bsel;
   if (p.Dqk != D || p.Dv != D || p.group != G || p.block_size != BS || p.Hkv % p.Hidx != 0)

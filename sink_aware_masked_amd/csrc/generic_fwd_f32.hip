@@ -76,7 +76,7 @@ __global__ __launch_bounds__(256) void generic_fwd_f32(const Params p) {
     const int s = find_segment(p.cu, p.num_seqs, i);
     const int start = p.cu[s], end = p.cu[s + 1];
     key0 = start;
-    const int lo = max(start, i - p.window), hi = min(end - 1, i + p.window);
+    const int lo = i - min(p.window, i - start), hi = i + min(p.window, end - 1 - i);  // no overflow
     for (int j = lo; j <= hi; ++j) visit(j);
   } else if (MASK == kMaskTopk) {
     const int32_t* idx = p.topk_idx + (int64_t)i * p.topk_row;
@@ -108,6 +108,8 @@ __global__ __launch_bounds__(256) void generic_fwd_f32(const Params p) {
   }
   if (lane == 0) p.lse[(int64_t)h * p.T + i] = lse_natural(m2, l);
 }
+
+int64_t generic_f32_items(const Params& p) { return ((int64_t)p.T * p.Hq + 3) / 4 * 256; }
 
 template <int MASK>
 static hipError_t launch_generic_m(const Params& p, int sink, hipStream_t st) {

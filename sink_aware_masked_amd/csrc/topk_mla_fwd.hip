@@ -278,6 +278,8 @@ void topk_mla_fwd_bf16(const Params p) {
   }
 }
 
+int64_t topk_mla_bf16_items(const Params& p) { return 2 * (int64_t)p.T * (p.Hq / mla::HPB) * 256; }
+
 hipError_t launch_topk_mla_bf16(const Params& p, int sink, hipStream_t st) {
   if (p.Dqk != mla::DQK || p.Dv != mla::DV || p.Hq % mla::HPB != 0) return hipErrorInvalidValue;
   const dim3 grid((unsigned)(2 * (int64_t)p.T * (p.Hq / mla::HPB))), block(256);  // two passes, see above

@@ -119,16 +119,17 @@ void window_fwd_bf16(const Params p) {
   // so no vector load is pending once the ring is in flight).
   const int sa = find_segment(p.cu, p.num_seqs, r0);
   const int sb = find_segment(p.cu, p.num_seqs, rlast);
-  const int kmin = max(__ldg(p.cu + sa), r0 - p.window);
-  const int kmax = min(__ldg(p.cu + sb + 1) - 1, rlast + p.window);
+  // bounds as offsets that cannot overflow: max(start, r - W) = r - min(W, r - start)
+  const int kmin = r0 - min(p.window, r0 - __ldg(p.cu + sa));
+  const int kmax = rlast + min(p.window, __ldg(p.cu + sb + 1) - 1 - rlast);
   const int ri = min(r0w + n, rlast);  // this lane's row (clamped past the end)
   int start = 0, end = 1;
   for (int s = sa; s <= sb; ++s) {
     const int cs = __ldg(p.cu + s), ce = __ldg(p.cu + s + 1);
     if (ri >= cs && ri < ce) { start = cs; end = ce; }
   }
-  const int lo = max(start, ri - p.window);
-  const int hi = min(end - 1, ri + p.window);
+  const int lo = ri - min(p.window, ri - start);
+  const int hi = ri + min(p.window, end - 1 - ri);
   // Rows, lo and hi are non-decreasing along the lanes 0..31.  Wave band
   // [wlo, whi]; interior [ilo, ihi] valid for every row of the wave; key-0
   // positions (sequence starts) of the wave lie in [k0a, k0b].
@@ -369,6 +370,14 @@ void window_fwd_bf16(const Params p) {
   }
   const int i = r0w + n;
   if (hf == 0 && i <= rlast) p.lse[(int64_t)h * p.T + i] = lse_natural(m2, lsum);
+}
+
+// Work items of one launch (workgroups x 256 lanes); every head dim uses
+// 128-row tiles.
+int64_t window_bf16_items(const Params& p) {
+  static_assert(WinCfg<64>::BM == 128 && WinCfg<80>::BM == 128 && WinCfg<96>::BM == 128 &&
+                WinCfg<128>::BM == 128, "one tile height");
+  return ((int64_t)p.T + 127) / 128 * p.Hq * 256;
 }
 
 template <int D>

@@ -7,8 +7,8 @@ show that every planted mistake fails at least one pin.
 Sources for what is pinned:
 * "[Bugfix][MiMo] Apply vision attention sinks in the window attention path":
   the key-0 closed form p0 = exp(logit0 - lse), out' = (out + p0 (e^s - 1) v0)
-  / (1 + p0 (e^s - 1)); only the first window_size + 1 queries of a sequence
-  see its key 0; passing the sink as a null logit is a different operation.
+  / (1 + p0 (e^s - 1)); the rows that reach key 0 are a sequence's first W + 1
+  (so only they change); a null-logit sink is a different operation.
 * "Apply DeepSeek-V4 attn_sink in the XPU sparse-MLA Triton kernel": the sink
   joins the softmax denominator only, the LSE covers the selected keys only,
   a sink of -inf is a no-op, and short rows must differ from the no-sink result.

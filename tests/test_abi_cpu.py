@@ -360,3 +360,133 @@ def test_row_stride_limit_of_a_64_row_tile(sam):
         ok = dict(base, **{key: strided(base[key], (1 << 24) - 64)})
         assert check(sam, ok) == 0, key
         _bad(sam, base, "ATTN_ERR_RANGE", **{key: strided(base[key], 1 << 24)})
+
+
+# ---------------------------------------------------------------- binding argument checks
+# The binding passes cu_seqlens, sinks, lse, kv_scale and workspace to the C
+# ABI as bare pointers; it must refuse a wrong device, dtype or size before any
+# call reaches the library (a host pointer or an undersized buffer would reach
+# a kernel otherwise).
+
+def _fwd_args(dev="cpu"):
+    import torch
+    T, Hq, Hkv, D = 8, 4, 2, 64
+    q = torch.zeros((T, Hq, D), dtype=torch.bfloat16, device=dev)
+    k = torch.zeros((T, Hkv, D), dtype=torch.bfloat16, device=dev)
+    v = torch.zeros((T, Hkv, D), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((T, Hq, D), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((Hq, T), dtype=torch.float32, device=dev)
+    cu = torch.tensor([0, 3, 8], dtype=torch.int32, device=dev)
+    sinks = torch.zeros(Hq, dtype=torch.float32, device=dev)
+    return dict(q=q, k=k, v=v, cu_seqlens=cu, mask_kind="window", window=2, scale=0.125,
+                sinks=sinks, sink_mode="key0_bias", out=out, lse=lse)
+
+
+@pytest.mark.parametrize("bad", ["cu_int64", "lse_bf16", "lse_short", "sinks_short", "sinks_missing",
+                                 "sinks_f64", "lse_strided", "cpu_tensors"])
+def test_binding_refuses_bad_buffers(sam, bad):
+    import torch
+    a = _fwd_args()
+    if bad == "cu_int64":
+        a["cu_seqlens"] = a["cu_seqlens"].to(torch.int64)
+        err = TypeError
+    elif bad == "lse_bf16":
+        a["lse"] = a["lse"].to(torch.bfloat16)
+        err = TypeError
+    elif bad == "lse_short":
+        a["lse"] = a["lse"][:, :4]
+        err = ValueError
+    elif bad == "sinks_short":
+        a["sinks"] = a["sinks"][:2]
+        err = ValueError
+    elif bad == "sinks_missing":
+        a["sinks"] = None
+        err = ValueError
+    elif bad == "sinks_f64":
+        a["sinks"] = a["sinks"].double()
+        err = TypeError
+    elif bad == "lse_strided":
+        a["lse"] = torch.empty((a["lse"].shape[1], a["lse"].shape[0]), dtype=torch.float32).t()
+        err = ValueError
+    else:  # everything consistent, but in host memory: the kernels need device memory
+        err = ValueError
+    with pytest.raises(err):
+        sam.fwd(**a)
+    with pytest.raises(err):
+        sam.prepared_fwd(**a)
+
+
+def test_binding_refuses_mixed_devices(sam):
+    import torch
+    a = _fwd_args()
+    meta = {k: (v.to("meta") if isinstance(v, torch.Tensor) and k in ("q", "k", "v", "out") else v)
+            for k, v in a.items()}
+    with pytest.raises(ValueError, match="is on"):
+        sam.fwd(**meta)
+
+
+def test_binding_refuses_bad_decode_buffers(sam):
+    import torch
+    T, Hq, Tk = 2, 64, 16
+    q = torch.zeros((T, Hq, 576), dtype=torch.bfloat16)
+    kv = torch.zeros((Tk, 1, 576), dtype=torch.uint8).view(torch.float8_e4m3fn)
+    idx = torch.zeros((T, 4), dtype=torch.int32)
+    out = torch.empty((T, Hq, 512), dtype=torch.bfloat16)
+    lse = torch.empty((Hq, T), dtype=torch.float32)
+    ws = torch.empty(1 << 20, dtype=torch.uint8)
+    with pytest.raises(TypeError):   # kv_scale in fp64
+        sam.attn_sink_mla_decode_fp8(q, kv, torch.ones(Tk, dtype=torch.float64), idx, None, "none", 0.1,
+                                     out, lse, ws)
+    with pytest.raises(ValueError):  # one scale short
+        sam.attn_sink_mla_decode_fp8(q, kv, torch.ones(Tk - 1), idx, None, "none", 0.1, out, lse, ws)
+    with pytest.raises(ValueError):  # null_logit without sinks
+        sam.attn_sink_mla_decode_fp8(q, kv, torch.ones(Tk), idx, None, "null_logit", 0.1, out, lse, ws)
+
+
+def test_binding_refuses_bad_merge_buffers(sam):
+    import torch
+    T, Hq, Dv = 4, 2, 16
+    parts = [(torch.zeros((T, Hq, Dv)), torch.zeros((Hq, T))) for _ in range(2)]
+    out = torch.empty((T, Hq, Dv))
+    with pytest.raises(TypeError):   # a partial LSE in bf16
+        sam.attn_sink_merge([parts[0], (parts[1][0], parts[1][1].bfloat16())], None, "none", out,
+                            torch.empty((Hq, T)))
+    with pytest.raises(ValueError):  # output LSE too small
+        sam.attn_sink_merge(parts, None, "none", out, torch.empty((Hq, T - 1)))
+
+
+def _fake(shape, dtype=0, data=1 << 20):
+    """Host-side descriptor of a dense array that is never touched."""
+    import sink_aware_masked_amd as m
+    stride, acc = [], 1
+    for n in reversed(shape):
+        stride.insert(0, acc)
+        acc *= n
+    return m.desc(None, data=data, dtype=dtype, shape=tuple(shape), stride=tuple(stride))
+
+
+def test_grid_limit_boundary(sam):
+    """The window launch uses ceil(T / 128) * Hq workgroups of 256 lanes; a call
+    whose grid exceeds 2^32 - 1 work items is refused by the check (not at
+    launch), and the largest one that fits is accepted."""
+    def win(T, Hq=1):
+        q, out = _fake((T, Hq, 64)), _fake((T, Hq, 64))
+        k, v = _fake((T, 1, 64)), _fake((T, 1, 64))
+        return sam.attn_sink_check(q, k, v, 1 << 20, 1, "window", {"window": 4}, None, "none", 0.125, out, 1 << 20)
+    fits = 128 * ((1 << 24) - 1)
+    assert win(fits) == 0
+    assert sam.STATUS[win(fits + 1)] == "ATTN_ERR_RANGE"
+    assert sam.STATUS[win(fits // 2 + 1, Hq=2)] == "ATTN_ERR_RANGE"
+
+
+def test_unbounded_window_accepted(sam):
+    """W = INT32_MAX (an unbounded window) is valid on both precisions: the
+    library clamps it to T, so no row + W sum leaves the int32 range."""
+    for dt in (torch.bfloat16, torch.float32):
+        a = window_args(D=64, dtype=dt)
+        a["mask"] = {"window": 2 ** 31 - 1}
+        assert check(sam, a) == 0
+    k0 = window_args(D=64)
+    rc = sam.attn_sink_key0_correct_check(k0["q"], k0["k"], k0["v"], k0["cu_seqlens"], 2, 2 ** 31 - 1,
+                                          k0["sinks"], 0.1, k0["out"], k0["lse"])
+    assert rc == 0

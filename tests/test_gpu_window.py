@@ -44,6 +44,7 @@ EDGE = [
     ([333], 1, 1, 80, 17, "none"),                    # one head, ragged tail tile
     ([64, 64], 16, 16, 80, 64, "key0_bias"),          # exactly one tile per sequence
     ([2047, 3, 70], 8, 1, 64, 100, "null_logit"),     # MQA, W larger than a tile
+    ([50, 3, 200], 4, 2, 80, 2 ** 31 - 1, "key0_bias"),  # W = INT32_MAX: unbounded window, no int32 wrap
 ]
 
 
@@ -155,3 +156,13 @@ def test_window_kv_rows_past_2_31():
     assert rel <= G.BF16_REL_L2 and dl <= G.BF16_LSE_ABS
     del kb, vb, k, v
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_window_unbounded_int32_max(dtype):
+    """An 'unbounded' window W = 2^31 - 1 on both instances equals full
+    attention within each sequence (the library clamps W to T; row +- W never
+    wraps in int32)."""
+    case = W.window_case([50, 3, 200, 1], 4, 2, 64, 2 ** 31 - 1, dtype=dtype, sink_mode="null_logit",
+                         sink_range=(-2, 2), seed=11)
+    G.assert_parity(case, label=f"window W=INT32_MAX {dtype}")
