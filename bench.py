@@ -6,11 +6,14 @@ enumeration, K/V staging, logits, online softmax, output accumulation and the
 sink epilogue -- one kernel launch) over one batch of seeded synthetic input
 that is already resident in HBM.
 
-Default workload (no flags): the MiMo vision window block -- 4096 tokens
-packed as 2 x 2048, 16 heads, head dim 80, window 64, bf16, key0_bias sinks
-drawn from U(-0.1, 0.6) -- the shape of the timing paragraph of the vLLM page
-"[Bugfix][MiMo] Apply vision attention sinks in the window attention path".
-Other workloads: --workload window_16k | mla_topk | blocksparse_32k.
+Default workload (no flags): the MiniMax-M3-style block-sparse layer of the
+NeMo AutoModel "cp_sparse_attn" page (_flex_sparse_attention: selected block
+and token-causal and same document) -- 32768 tokens in 4 packed documents,
+32 query / 8 kv heads, head dim 128, 64-token key blocks, each query its own
+diagonal block plus 15 random earlier blocks of its document, bf16, null_logit
+sinks from U(-2, 2) -- the largest workload that fits one GPU; the same layer
+without a sink is timed too and reported as a ratio (sink_vs_none).
+Other workloads: --workload window_4k | window_16k | mla_topk | mla_decode_fp8.
 --compare-unfused (window workloads) also times the page's unfused design (no-sink
 kernel + closed-form key-0 correction); --measure-merge (mla_topk) times the
 top-k lists split in two halves, each through the no-sink kernel, merged by LSE
@@ -22,7 +25,9 @@ Prints ONE JSON line:
   value      useful TFLOP/s of the whole job = 2 (Dqk + Dv) sum |S(i,h)| / wall time
   roofline   the kernel against its binding roof, from HIP events on the
              launch stream around the timed launches (algorithmic bytes or
-             useful flops per launch / average launch duration)
+             useful flops per launch / average launch duration); also the
+             median, p10 and p90 of per-launch durations (HIP events around
+             each of `steps` further launches)
   cpu_baseline  the CPU oracle (C, fp64, OpenMP) on a bounded row sample of
              the same workload, in the same unit
 Cold cache: the step rotates over enough input sets to exceed the 256 MB
@@ -49,7 +54,9 @@ PEAK_MFMA_BF16_TFS = 2500.0  # MI355X dense bf16 MFMA, published
 MALL_BYTES = 256 << 20       # Infinity Cache
 
 # The pages' timing context (H100, FlashAttention varlen + the unfused key-0
-# correction): ms per call for the same window workloads.
+# correction): ms per call for the same window workloads.  Another machine and
+# another design: reported beside the result (page_context), never as its
+# baseline.
 PAGE_MS = {("window_4k", "key0_bias"): 0.248, ("window_4k", "none"): 0.038,
            ("window_16k", "key0_bias"): 0.289, ("window_16k", "none"): 0.134}
 
@@ -206,6 +213,12 @@ def time_gpu(case, sets_n, steps, warmup, use_graph=True):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     kern_ms = ev0.elapsed_time(ev1) / steps                    # average launch duration
+    counter = [0]
+
+    def one():
+        eager[counter[0] % sets_n]()
+        counter[0] += 1
+    stats = launch_stats(one, steps)
     if use_graph:  # a replayed launch must reproduce the eager result bit for bit
         ref_out = torch.empty_like(sets[0]["out"])
         ref_lse = torch.empty_like(sets[0]["lse"])
@@ -213,7 +226,23 @@ def time_gpu(case, sets_n, steps, warmup, use_graph=True):
         torch.cuda.synchronize()
         assert torch.equal(ref_out, sets[0]["out"]) and torch.equal(ref_lse, sets[0]["lse"]), \
             "graph replay differs from the eager launch"
-    return wall * 1e3 / steps, kern_ms, sets[0]
+    return wall * 1e3 / steps, kern_ms, sets[0], stats
+
+
+def launch_stats(fn, n):
+    """Median, p10 and p90 (ms) of n launches of fn, each bracketed by HIP
+    events on torch's current stream (the stream the binding launches on)."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    torch.cuda.synchronize()
+    for e0, e1 in evs:
+        e0.record()
+        fn()
+        e1.record()
+    torch.cuda.synchronize()
+    t = np.array([e0.elapsed_time(e1) for e0, e1 in evs])
+    return {"launches": int(n), "median_ms": float(np.median(t)), "p10_ms": float(np.percentile(t, 10)),
+            "p90_ms": float(np.percentile(t, 90))}
 
 
 def graph_ms(step, steps, warmup):
@@ -381,12 +410,14 @@ def cpu_baseline(case, pairs_row, dqk_dv, budget_s, out_dev, lse_dev):
     ref_n = np.linalg.norm(ref_o, axis=2)
     nz = fin & (ref_n > 0)
     rel = float((np.linalg.norm(out - ref_o, axis=2)[nz] / ref_n[nz]).max()) if nz.any() else 0.0
+    # the pages' statistic: one relative L2 over the whole output tensor
+    tens = float(np.linalg.norm(out - ref_o) / np.linalg.norm(ref_o)) if np.linalg.norm(ref_o) > 0 else 0.0
     dl = float(np.abs(lse.T[fin] - ref_l.T[fin]).max()) if fin.any() else 0.0
     assert np.all(out[~fin] == 0.0) and np.all(np.isneginf(lse.T[~fin]))
     return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
             "sample": f"{n} of {T} query rows (all heads), seeded, x{reps} passes; {secs:.1f} s wall; fp64 C enumerator",
             "ms_per_call_equiv": secs / reps * 1e3 * float(pairs_row.sum()) / float(pairs_row[rows].sum())}, \
-        {"max_rel_l2": rel, "lse_max_abs": dl, "rows_checked": n}
+        {"max_rel_l2": rel, "tensor_rel_l2": tens, "lse_max_abs": dl, "rows_checked": n}
 
 
 def bench_decode(args, case):
@@ -455,6 +486,7 @@ def bench_decode(args, case):
                                "sample": f"{len(rows)} of {T} rows (all heads), seeded, x{reps} passes; {secs:.1f} s wall; "
                                          "fp64 C enumerator after an fp64 NumPy dequantization of the cache"}
         res["parity_sample"] = {"max_rel_l2": float((num[nz] / den[nz]).max()),
+                                "tensor_rel_l2": float(np.linalg.norm(out - ref_o) / np.linalg.norm(ref_o)),
                                 "lse_max_abs": float(np.abs(d["lse"].cpu().numpy()[:, rows] - ref_l).max()),
                                 "rows_checked": int(len(rows))}
     else:
@@ -503,7 +535,37 @@ def device_facts(copy_bytes: int = 1 << 30, reps: int = 10) -> dict:
     torch.cuda.empty_cache()
     return {"name": props.name, "compute_units": props.multi_processor_count,
             "arch": getattr(props, "gcnArchName", None), "copy_bytes": 2 * copy_bytes,
-            "copy_GBps_torch": torch_gbs, "copy_GBps_row_gather": rows_gbs}
+            "copy_GBps_torch": torch_gbs, "copy_GBps_row_gather": rows_gbs, "latent_gather": latent_gather()}
+
+
+def latent_gather(rows: int = 65536, row_bytes: int = 1152, n: int = 1 << 18, reps: int = 10) -> dict:
+    """The access pattern of the sparse-MLA kernel's gathered stream, timed
+    through the library's row gather (attn_sink_cp_permute_rows, gather mode):
+    n uniformly random 1152-byte rows (one bf16 latent row of 576 values) of a
+    65536-row table, written densely.  read_GBps counts the gathered bytes
+    only; rw_GBps adds the dense writes, which the attention kernel does not
+    make."""
+    import torch
+    import sink_aware_masked_amd as sam
+    tbl = torch.randint(0, 255, (rows, row_bytes), dtype=torch.uint8, device="cuda:0")
+    g = torch.Generator(device="cpu").manual_seed(7)
+    idx = torch.randint(0, rows, (n,), generator=g, dtype=torch.int64).to("cuda:0")
+    dst = torch.empty((n, row_bytes), dtype=torch.uint8, device="cuda:0")
+    for _ in range(2):
+        sam.attn_sink_cp_permute_rows(tbl, idx, False, dst)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        sam.attn_sink_cp_permute_rows(tbl, idx, False, dst)
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / reps * 1e-3
+    probe = torch.randint(0, n, (64,), generator=g)
+    assert torch.equal(dst[probe.to("cuda:0")], tbl[idx[probe.to("cuda:0")]])
+    del tbl, dst, idx
+    torch.cuda.empty_cache()
+    return {"table_rows": rows, "row_bytes": row_bytes, "gathered_rows": n, "ms": t * 1e3,
+            "read_GBps": n * row_bytes / t / 1e9, "rw_GBps": 2 * n * row_bytes / t / 1e9}
 
 
 def main(argv=None):
@@ -511,16 +573,19 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="window_4k",
+    ap.add_argument("--workload", default="blocksparse_32k",
                     choices=["window_4k", "window_16k", "mla_topk", "blocksparse_32k", "blocksparse_32k_coherent",
                              "mla_decode_fp8"])
-    ap.add_argument("--sink-mode", default=None, choices=[None, "none", "key0_bias", "null_logit"])
+    ap.add_argument("--sink-mode", default=None, choices=[None, "none", "key0_bias", "null_logit"],
+                    help="default: the workload's own (key0_bias for window, null_logit for the others; "
+                         "blocksparse_32k: null_logit)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--gqa", action="store_true", help="window_4k: the GQA variant (16 query heads over 4 kv heads)")
     ap.add_argument("--sets", type=int, default=0, help="input sets to rotate (0: enough to exceed the MALL)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle sample budget (0: skip)")
     ap.add_argument("--compare-sink-none", action="store_true",
-                    help="also time the same workload without a sink and report the ratio")
+                    help="also time the same workload without a sink and report the ratio "
+                         "(always on for the default block-sparse workload)")
     ap.add_argument("--compare-unfused", action="store_true",
                     help="window workloads: also time the no-sink kernel + closed-form key-0 correction")
     ap.add_argument("--measure-merge", action="store_true",
@@ -550,8 +615,12 @@ def main(argv=None):
         print("--gqa applies to the window_4k workload only", file=sys.stderr)
         return 2
     workload = args.workload + ("_gqa" if args.gqa else "")
+    sink_mode = args.sink_mode
+    if sink_mode is None and args.workload.startswith("blocksparse_32k"):
+        sink_mode = "null_logit"      # the layer's sink pass; the no-sink pass is timed beside it
+        args.compare_sink_none = True
     log(f"[bench] building workload {workload} seed {args.seed}")
-    case = build_case(args.workload, args.seed, args.sink_mode, args.gqa)
+    case = build_case(args.workload, args.seed, sink_mode, args.gqa)
     if case["mask_kind"] == "topk_fp8":
         return bench_decode(args, case)
     prow = pairs_per_row(case)
@@ -571,7 +640,7 @@ def main(argv=None):
         log(f"[bench] calibration copy of {args.calibrate_copy} MiB done")
 
     log(f"[bench] timing {args.steps} steps after {args.warmup} warmup")
-    ms, kern_ms, dev0 = time_gpu(case, sets_n, args.steps, args.warmup, use_graph=not args.no_graph)
+    ms, kern_ms, dev0, stats = time_gpu(case, sets_n, args.steps, args.warmup, use_graph=not args.no_graph)
     kind = case["mask_kind"]
     bound = "hbm" if kind == "window" else "mfma"
     if bound == "hbm":
@@ -584,6 +653,7 @@ def main(argv=None):
     roof["traffic"] = load_traffic(workload + ":" + case["sink_mode"], kind)
     roof.update(both_roofs(F, B, kern_ms))
     roof["kernel_ms"] = kern_ms
+    roof["launch_ms"] = stats
     roof["algorithmic_bytes"] = B
     roof["useful_flops"] = F
 
@@ -591,14 +661,21 @@ def main(argv=None):
     page = PAGE_MS.get((workload, case["sink_mode"]))
     res = {"metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
-           "vs_baseline": (page / ms) if page else None, "dtype": case["dtype"], "data": "synthetic",
+           "vs_baseline": None, "dtype": case["dtype"], "data": "synthetic",
            "config": describe(workload, case, sets_n), "roofline": roof, "device": device_facts()}
+    if page:
+        res["page_context"] = {"page_ms": page, "page_over_ours": page / ms,
+                               "note": "the MiMo page's H100 time for the same shape (FlashAttention varlen"
+                                       + (" + the unfused key-0 correction" if case["sink_mode"] == "key0_bias" else "")
+                                       + "); another machine and design, context only"}
 
     if args.compare_sink_none and case["sink_mode"] != "none":
         base = dict(case, sink_mode="none", sinks=None)
-        ms0, kern0, _ = time_gpu(base, sets_n, args.steps, args.warmup, use_graph=not args.no_graph)
+        ms0, kern0, _, stats0 = time_gpu(base, sets_n, args.steps, args.warmup, use_graph=not args.no_graph)
         res["sink_vs_none"] = {"kernel_ms_sink": kern_ms, "kernel_ms_none": kern0,
-                               "ratio": kern_ms / kern0, "ms_per_step_none": ms0}
+                               "ratio": kern_ms / kern0, "ms_per_step_none": ms0,
+                               "median_ms_sink": stats["median_ms"], "median_ms_none": stats0["median_ms"],
+                               "median_ratio": stats["median_ms"] / stats0["median_ms"]}
 
     if args.compare_unfused:
         if kind != "window" or case["sink_mode"] != "key0_bias":

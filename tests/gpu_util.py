@@ -37,6 +37,13 @@ def oracle_run(case: dict, rows=None, **over):
     return P.run(oracle.attn_ref, case, rows=rows, **over)
 
 
+def tensor_rel_l2(out, ref_out) -> float:
+    """One relative L2 over the whole output tensor (the pages' error
+    statistic, reported beside the per-row maximum that gates)."""
+    den = float(np.linalg.norm(ref_out))
+    return float(np.linalg.norm(out - ref_out)) / den if den > 0 else 0.0
+
+
 def compare(out, lse, ref_out, ref_lse):
     """Returns (max rel L2 over non-empty (row, head), max |dLSE| over finite).
     Asserts that rows the oracle calls empty are exactly 0 / -inf."""
@@ -64,7 +71,8 @@ def assert_parity(case: dict, rows=None, label="", **over):
         out, lse = out[rows], lse[:, rows]
     rel, dl = compare(out, lse, ref_out, ref_lse)
     tr, tl = tolerances(case)
-    say(f"[parity] {label or case['name']}: max rel L2 {rel:.3e} (<= {tr}), lse max abs {dl:.3e} (<= {tl})")
+    say(f"[parity] {label or case['name']}: max rel L2 {rel:.3e} (<= {tr}), tensor rel L2 "
+        f"{tensor_rel_l2(out, ref_out):.3e}, lse max abs {dl:.3e} (<= {tl})")
     assert rel <= tr and dl <= tl, (rel, dl)
     return out, lse
 

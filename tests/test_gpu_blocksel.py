@@ -15,12 +15,13 @@ pytestmark = pytest.mark.gpu
 
 @pytest.mark.parametrize("seed", [0, 1, 2])
 @pytest.mark.parametrize("sink", ["none", "null_logit"])
-def test_blocksparse_32k_sampled(seed, sink):
+def test_blocksparse_32k(seed, sink):
     """Full-size block-sparse workload (32768 tokens, 4 documents, 32/8 heads,
-    d128, 64-token blocks) in the benchmark's launch configuration; oracle on
-    sampled rows including every document's first and last tokens."""
+    d128, 64-token blocks) in the benchmark's launch configuration: seed 0 is
+    compared on every row and head, seeds 1 and 2 on sampled rows including
+    every document's first and last tokens."""
     case = W.make_workload("blocksparse_32k", seed=seed, sink_mode=sink)
-    rows = G.sample_rows(case, 400, seed=seed)
+    rows = None if seed == 0 else G.sample_rows(case, 400, seed=seed)
     G.assert_parity(case, rows=rows, label=f"blocksparse_32k {sink} seed{seed}")
 
 

@@ -28,9 +28,11 @@ def test_window_4k(seed, variant):
 
 @pytest.mark.parametrize("seed", [0, 1, 2])
 @pytest.mark.parametrize("sink", ["key0_bias", "none"])
-def test_window_16k_sampled(seed, sink):
+def test_window_16k(seed, sink):
+    """16384-token window workload: seed 0 on every row, seeds 1 and 2 on
+    sampled rows (segment ends included)."""
     case = W.make_workload("window_16k", seed=seed, sink_mode=sink)
-    rows = G.sample_rows(case, 3000, seed=seed)
+    rows = None if seed == 0 else G.sample_rows(case, 3000, seed=seed)
     G.assert_parity(case, rows=rows, label=f"window_16k {sink} seed{seed}")
 
 
