@@ -45,9 +45,12 @@
  *   - The caller owns every buffer, including the one scratch buffer (the fp8
  *     decode's workspace).  The library allocates nothing and keeps no
  *     mutable global state: calls are reentrant and may run concurrently on
- *     different streams.  Inputs are read only.  attn_sink_fwd and
- *     attn_sink_merge fully write out and lse (rows with an empty key set get
- *     out = 0 and lse = -inf); attn_sink_key0_correct updates them in place.
+ *     different streams.  The one exception is the allocation-free decode
+ *     (attn_sink_mla_decode_fp8_noalloc), whose scratch is a static device
+ *     array shared by all its calls on a GPU.  Inputs are read only.
+ *     attn_sink_fwd and attn_sink_merge fully write out and lse (rows with an
+ *     empty key set get out = 0 and lse = -inf); attn_sink_key0_correct
+ *     updates them in place.
  *   - Each call enqueues a single kernel launch on `stream` (the fp8 decode
  *     two); no call ever synchronises or reads device memory from the host.
  *   - Errors are returned as negative attn_status codes.  Every argument error
@@ -364,6 +367,26 @@ int attn_sink_mla_decode_fp8_check(const attn_tensor* q, const attn_tensor* kv, 
  * top-k lists of length topk (host-only; ATTN_ERR_RANGE if Hq is not a
  * positive multiple of 64). */
 int attn_sink_mla_decode_fp8_workspace(int64_t T, int64_t Hq, int64_t topk, int64_t* bytes);
+
+/*
+ * attn_sink_mla_decode_fp8_noalloc -- the same decode as
+ * attn_sink_mla_decode_fp8 (same arguments and results, same two kernels),
+ * for callers that cannot allocate or pass device memory around: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * It takes no workspace and allocates nothing; its fp32 partial results go
+ * to a static device array of the library (ATTN_SINK_DECODE_SCRATCH_BYTES
+ * per GPU, held from the library's load until the process ends).  The
+ * scratch of the CURRENT device is used: call it with the device current
+ * that `stream` belongs to.  Every call on one GPU shares that array, so
+ * calls that overlap on one GPU (other streams, other host threads) race;
+ * serialise them.  A call whose partials need more than the limit (see
+ * attn_sink_mla_decode_fp8_workspace for the size) returns ATTN_ERR_RANGE
+ * before touching the device; otherwise errors as for attn_sink_mla_decode_fp8.
+ */
+#define ATTN_SINK_DECODE_SCRATCH_BYTES ((int64_t)96 << 20)
+int attn_sink_mla_decode_fp8_noalloc(const attn_tensor* q, const attn_tensor* kv, const float* kv_scale,
+                                     const attn_tensor* topk_idx, const float* sinks, int32_t sink_mode, float scale,
+                                     const attn_tensor* out, float* lse, hipStream_t stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* attn_sink_strerror(int status);

@@ -33,7 +33,9 @@ EXPORTS = ("attn_sink_fwd", "attn_sink_check", "attn_sink_key0_correct", "attn_s
            "attn_sink_merge", "attn_sink_merge_check", "attn_sink_cp_slots", "attn_sink_cp_slots_check",
            "attn_sink_cp_permute_rows", "attn_sink_cp_permute_rows_check", "attn_sink_cp_documents",
            "attn_sink_cp_documents_check", "attn_sink_mla_decode_fp8", "attn_sink_mla_decode_fp8_check",
-           "attn_sink_mla_decode_fp8_workspace", "attn_sink_strerror", "attn_sink_abi_version")
+           "attn_sink_mla_decode_fp8_workspace", "attn_sink_mla_decode_fp8_noalloc", "attn_sink_strerror",
+           "attn_sink_abi_version")
+DECODE_SCRATCH_BYTES = 96 << 20
 MERGE_MAX_PARTS = 8
 
 
@@ -85,6 +87,8 @@ _lib.attn_sink_mla_decode_fp8.restype = ctypes.c_int
 _lib.attn_sink_mla_decode_fp8.argtypes = _DEC + [_P]
 _lib.attn_sink_mla_decode_fp8_check.restype = ctypes.c_int
 _lib.attn_sink_mla_decode_fp8_check.argtypes = _DEC
+_lib.attn_sink_mla_decode_fp8_noalloc.restype = ctypes.c_int
+_lib.attn_sink_mla_decode_fp8_noalloc.argtypes = [_T, _T, _P, _T, _P, _I32, ctypes.c_float, _T, _P, _P]
 _lib.attn_sink_mla_decode_fp8_workspace.restype = ctypes.c_int
 _lib.attn_sink_mla_decode_fp8_workspace.argtypes = [_I64, _I64, _I64, ctypes.POINTER(ctypes.c_int64)]
 _lib.attn_sink_strerror.restype = ctypes.c_char_p
@@ -413,7 +417,7 @@ def attn_sink_cp_documents(positions, doc_ids=None, cu_seqlens=None, num_docs=No
     import torch
     dev = positions.device
     _aux("positions", positions, torch.int64, positions.numel(), dev)
-    _aux("doc_ids", doc_ids, torch.int32, positions.numel(), dev, optional=True)
+    _aux("doc_ids", doc_ids, torch.int32, positions.numel(), dev, optional=True, at_least=True)
     _aux("num_docs", num_docs, torch.int32, 1, dev, optional=True)
     if cu_seqlens is not None:
         _aux("cu_seqlens", cu_seqlens, torch.int32, max(cu_seqlens.numel(), 1), dev)
@@ -462,6 +466,28 @@ def attn_sink_mla_decode_fp8(q, kv, kv_scale, topk_idx, sinks, sink_mode, scale,
     _check_rc(_lib.attn_sink_mla_decode_fp8(ctypes.byref(dq), ctypes.byref(dk), _ptr(kv_scale), ctypes.byref(di),
                                             _ptr(sinks), sm, float(scale), ctypes.byref(do), _ptr(lse),
                                             _ptr(workspace), int(nbytes), ctypes.c_void_p(_stream(stream, q.device))))
+
+
+def attn_sink_mla_decode_fp8_noalloc(q, kv, kv_scale, topk_idx, sinks, sink_mode, scale, out, lse,
+                                     stream=None) -> None:
+    """The fp8 sparse-MLA decode without a workspace: its partial results go to
+    the library's static per-GPU scratch (DECODE_SCRATCH_BYTES; larger calls
+    raise ATTN_ERR_RANGE).  Calls that overlap on one GPU race."""
+    import torch
+    sm = SINK_MODES[sink_mode] if isinstance(sink_mode, str) else int(sink_mode)
+    dev = q.device
+    T, Hq = q.shape[0], q.shape[1]
+    for name, t in (("kv", kv), ("topk_idx", topk_idx), ("out", out)):
+        _on_device(name, t, dev)
+    _aux("kv_scale", kv_scale, torch.float32, kv.shape[0], dev)
+    _aux("sinks", sinks, torch.float32, Hq, dev, optional=(sm != SINK_MODES["null_logit"]))
+    _aux("lse", lse, torch.float32, Hq * T, dev)
+    _need_gpu(q)
+    dq, dk, di, do = desc(q), desc(kv), desc(topk_idx), desc(out)
+    _check_rc(_lib.attn_sink_mla_decode_fp8_noalloc(ctypes.byref(dq), ctypes.byref(dk), _ptr(kv_scale),
+                                                    ctypes.byref(di), _ptr(sinks), sm, float(scale),
+                                                    ctypes.byref(do), _ptr(lse),
+                                                    ctypes.c_void_p(_stream(stream, q.device))))
 
 
 def decode_case_on_device(case: dict, device="cuda:0") -> dict:

@@ -591,6 +591,23 @@ ATTN_API int attn_sink_mla_decode_fp8(const attn_tensor* q, const attn_tensor* k
   return attn::launch_mla_decode_fp8(P, sink_mode, stream) == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
+ATTN_API int attn_sink_mla_decode_fp8_noalloc(const attn_tensor* q, const attn_tensor* kv, const float* kv_scale,
+                                              const attn_tensor* topk_idx, const float* sinks, int32_t sink_mode,
+                                              float scale, const attn_tensor* out, float* lse, hipStream_t stream) {
+  static_assert(attn::kDecodeScratchBytes == ATTN_SINK_DECODE_SCRATCH_BYTES, "scratch limit");
+  attn::DecodeParams P;
+  // validate against the scratch limit first (a placeholder address: no
+  // device access), so a refused call makes no HIP call at all
+  int rc = prepare_decode(q, kv, kv_scale, topk_idx, sinks, sink_mode, scale, out, lse,
+                          reinterpret_cast<const void*>((uintptr_t)256), attn::kDecodeScratchBytes, &P);
+  if (rc != ATTN_OK || P.T == 0) return rc;
+  void* base = nullptr;
+  if (attn::decode_scratch_address(&base) != hipSuccess) return ATTN_ERR_LAUNCH;
+  P.ws_out = static_cast<float*>(base);
+  P.ws_lse = P.ws_out + (int64_t)P.nsplit * P.T * P.Hq * 512;
+  return attn::launch_mla_decode_fp8(P, sink_mode, stream) == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
 ATTN_API const char* attn_sink_strerror(int status) {
   switch (status) {
     case ATTN_OK: return "ok";

@@ -20,7 +20,15 @@ struct DecodeParams {
   float scale_log2;
 };
 
+// Size of the static device scratch that holds the partial results of the
+// allocation-free entry point: 96 MiB, enough for the 128-row x 64-head
+// decode in 4 pieces (67.2 MB); larger calls are refused with ATTN_ERR_RANGE.
+constexpr int64_t kDecodeScratchBytes = (int64_t)96 << 20;
+
 int decode_splits(int64_t T, int64_t Hq, int64_t topk);
+// Device address of the static scratch on the current device (looked up once
+// per device, then cached).
+hipError_t decode_scratch_address(void** addr);
 int decode_split_len(int64_t topk, int nsplit);
 hipError_t launch_mla_decode_fp8(const DecodeParams& p, int sink, hipStream_t st);
 

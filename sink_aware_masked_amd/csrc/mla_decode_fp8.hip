@@ -12,7 +12,8 @@
 // every (row, 64-head group, piece) is its own workgroup (the partial kernel);
 // a second kernel merges the pieces by their LSEs and folds the sink in once
 // (the combine kernel, the same algebra as attn_sink_merge).  The partial
-// results are fp32 in a caller-provided workspace.
+// results are fp32 in a caller-provided workspace, or, for the
+// allocation-free entry point, in this file's static device scratch.
 //
 // Partial kernel, per 32-key tile: the 32 gathered fp8 rows (576 bytes each)
 // go straight from memory into a 2-stage LDS ring (direct-to-LDS loads), are
@@ -23,6 +24,8 @@
 // with the row scales of the tile held in LDS: the scale multiplies the logit
 // and the probability that weights the row's V, never the bf16 operands.
 #include "decode.hpp"
+
+#include <mutex>
 
 namespace attn {
 
@@ -306,6 +309,39 @@ __global__ __launch_bounds__(256) void mla_decode_fp8_combine(const DecodeParams
     *reinterpret_cast<bf16x8*>(static_cast<bf16*>(p.out) + (int64_t)i * p.o_row + (int64_t)h * p.o_head + 8 * d) = o;
     if (d == 0) p.lse[(int64_t)h * p.T + i] = lse;
   }
+}
+
+// ---------------------------------------------------------------- scratch of the allocation-free entry point
+// The partial results of attn_sink_mla_decode_fp8_noalloc live in this
+// file-scope device array (one copy per GPU, held for the life of the
+// process).  On the host `scratch` only names the symbol: its device address
+// is looked up once per device with hipGetSymbolAddress and that address is
+// what the kernels receive.  Every call on a GPU shares its copy; calls that
+// overlap on one GPU race.  Nothing in it needs to start at zero: the partial
+// kernel writes every (piece, row, head) slot before the combine reads it.
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t decode_scratch_address(void** addr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {  // first call on this device, with it current
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_addr[dev] = p;
+  }
+  *addr = g_scratch_addr[dev];
+  return hipSuccess;
 }
 
 int decode_splits(int64_t T, int64_t Hq, int64_t topk) {
