@@ -286,24 +286,38 @@ void blocksel_fwd_bf16(const Params p) {
   // documents up to 32*MAXW*64 tokens before the query block).
   for (int wb = blo >> 5; wb <= (bhi >> 5); wb += MAXW) {
     const int nwords = min(MAXW, (bhi >> 5) - wb + 1);
-    // ---- selection bits of the 64 queries, 32 blocks per word; the 32 byte
-    // loads of a word are independent (clamped index, masked bit)
+    // ---- selection bits of the 64 queries: a wave reads 64 consecutive
+    // table bytes of one query row per load (one cache line, coalesced), and
+    // the ballot of "byte != 0" is that row's bits for 64 blocks -- two words.
+    // Eight rows' loads are issued before their ballots.
     __syncthreads();  // the previous pass is done with qbits / blist / the ring
-    for (int t = tid; t < BS * nwords; t += 64 * NW) {
-      const int q = t / nwords, w = t - q * nwords;
-      uint32_t bits = 0;
-      const int qrow_idx = q0 + q;
-      if (qrow_idx <= qlast) {
-        const uint8_t* row = tab + (int64_t)qrow_idx * p.bsel_q;
-        const int blk0 = 32 * (wb + w);
+    {
+      const int nch = (nwords + 1) >> 1;  // 64-block chunks per row in this pass
+      const int items = BS * nch;
+      for (int it0 = wave; it0 < items; it0 += 8 * NW) {
+        uint8_t v[8];
+        int blk[8];
 #pragma unroll
-        for (int u = 0; u < 32; ++u) {
-          const int blk = blk0 + u;
-          const uint8_t v = row[min(max(blk, blo), bhi)];
-          bits |= (uint32_t)((v != 0) & (blk >= blo) & (blk <= bhi)) << u;
+        for (int u = 0; u < 8; ++u) {
+          const int it = it0 + u * NW;
+          const int q = it / nch, ch = it - q * nch;
+          blk[u] = 32 * wb + 64 * ch + lane;
+          const int qrow_idx = q0 + q;
+          v[u] = 0;
+          if (it < items && qrow_idx <= qlast)
+            v[u] = tab[(int64_t)qrow_idx * p.bsel_q + min(max(blk[u], blo), bhi)];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int it = it0 + u * NW;
+          const bool bit = (v[u] != 0) & (blk[u] >= blo) & (blk[u] <= bhi);
+          const uint64_t m = __ballot(bit);
+          if (it < items && lane < 2) {
+            const int q = it / nch, w = 2 * (it - q * nch) + lane;
+            if (w < nwords) qbits[q][w] = lane ? (uint32_t)(m >> 32) : (uint32_t)m;
+          }
         }
       }
-      qbits[q][w] = bits;
     }
     __syncthreads();
     // union over the 64 queries (a wave per word, OR-reduced across lanes),
