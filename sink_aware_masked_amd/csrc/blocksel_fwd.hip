@@ -30,22 +30,22 @@ namespace bsel {
 constexpr int D = 128;
 constexpr int G = 4;            // query heads per kv head
 constexpr int BS = 64;          // key block size = query tile
-constexpr int NW = 8;           // waves per workgroup (two per SIMD)
-constexpr int NB_PER_WAVE = 2;  // 16-column blocks per wave (8 queries x 4 heads)
+constexpr int NW = 16;          // waves per workgroup (four per SIMD)
+constexpr int NB_PER_WAVE = 1;  // 16-column blocks per wave (4 queries x 4 heads)
 constexpr int NQC = D / 32;     // 4 Q^T fragments per column block
 constexpr int NDV = D / 16;     // 8 output blocks
 constexpr int RCH = D / 8;      // 16 16-byte chunks per row
 constexpr int TILE_EL = BS * D; // bf16 elements of one K (or V) block
-constexpr int LDPW = BS * RCH / 64 / NW;  // 2 direct-to-LDS loads per wave per tensor
+constexpr int LDPW = BS * RCH / 64 / NW;  // 1 direct-to-LDS load per wave per tensor
 constexpr int MAXW = 32;        // selection words per query held in LDS per pass (1024 blocks)
 constexpr int NSTAGE = 4;       // LDS ring depth: three blocks in flight behind the one computed
 static_assert(NSTAGE >= 2 && NSTAGE <= 4, "the in-flight wait below covers up to two later blocks");
 }  // namespace bsel
 
-// 8 waves of 8 queries x 4 heads each, held to 256 registers, so two waves
-// share every SIMD and one's softmax or LDS waits overlap the other's MFMAs.
+// 16 waves of 4 queries x 4 heads each, held to 128 registers, so four waves
+// share every SIMD and one's softmax or LDS waits overlap the others' MFMAs.
 template <int SINK>
-__global__ __launch_bounds__(64 * bsel::NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(64 * bsel::NW) __attribute__((amdgpu_waves_per_eu(4, 4)))
 void blocksel_fwd_bf16(const Params p) {
   using namespace bsel;
   __shared__ __attribute__((aligned(16))) bf16 kvs[NSTAGE * 2 * TILE_EL];  // stages of (K block, V block)
@@ -355,18 +355,18 @@ void blocksel_fwd_bf16(const Params p) {
     // every wave is done with pair r - 1, whose stages then take pair r + 1
     // while pair r is computed.  Between barriers a wave runs through both
     // blocks, so a wave whose queries chose neither block of a pair costs the
-    // others one barrier instead of two.  Waves 0-3 issue their share of the
-    // next pair right after the barrier and waves 4-7 after their first
-    // block, so the two waves of a SIMD start the pair in different phases
-    // (one in its MFMAs while the other issues loads) and the loads of a pair
-    // reach the memory pipeline in two halves (2-3 % faster than all at once).
+    // others one barrier instead of two.  Waves 0-7 issue their share of the
+    // next pair right after the barrier and waves 8-15 after their first
+    // block, so the waves of a SIMD start the pair in two phases (some in
+    // their MFMAs while the others issue loads) and the loads of a pair reach
+    // the memory pipeline in two halves (2-3 % faster than all at once).
     const int npair = (nbl + 1) >> 1;
     auto issue_pair = [&](int r) {
 #pragma unroll
       for (int u = 0; u < 2; ++u)
         if (2 * r + u < nbl) issue(blist[2 * r + u], kvs + ((r & 1) * 2 + u) * 2 * TILE_EL);
     };
-    const bool late = (wave & 4) != 0;  // wave-uniform
+    const bool late = (wave & 8) != 0;  // wave-uniform
     issue_pair(0);
     for (int r = 0; r < npair; ++r) {
       wait_vmcnt<0>();
