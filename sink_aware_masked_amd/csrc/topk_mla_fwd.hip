@@ -169,7 +169,7 @@ void topk_mla_fwd_bf16(const Params p) {
     };
 
     // ---- one tile: S, online softmax with lazy rescale, PV
-    auto compute = [&](int t, const bf16* st) {
+    auto compute = [&](int t, const bf16* st, bf16* nxt, bool late_issue) {
       const int t0 = t * KT;
       float s[2][4];
 #pragma unroll
@@ -218,6 +218,7 @@ void topk_mla_fwd_bf16(const Params p) {
           pb[4 * sb + e] = static_cast<bf16>(pe);
         }
       lsum += ps;
+      if (late_issue) issue(t + 1, nxt);  // waves 2-3: the next tile's gathers after the softmax
       // V^T operands run VPIPE blocks ahead of the MFMAs that use them
       auto vload = [&](int n) {
         const bf16* v0 = st + vofs4[n & 3] + 2048 * (n >> 2);
@@ -235,11 +236,16 @@ void topk_mla_fwd_bf16(const Params p) {
 
     // tile t lives in stage t % 2; the loop is unrolled by the ring depth so
     // every LDS access names its stage array at compile time
+    // Waves 0-1 issue the next tile's gathers right after the barrier, waves
+    // 2-3 after their softmax, so a tile's 36 gather instructions reach the
+    // memory pipeline in two bursts (~1 % faster than one).
+    const bool late = wave >= 2;  // wave-uniform
     auto step = [&](int t, bf16* cur, bf16* next) {
       wait_vmcnt<0>();
       lds_barrier();  // tile t is in LDS for every wave; tile t-1's stage is free
-      if (t + 1 < ntiles) issue(t + 1, next);
-      compute(t, cur);
+      const bool more = t + 1 < ntiles;
+      if (more && !late) issue(t + 1, next);
+      compute(t, cur, next, more && late);
     };
     if (ntiles > 0) issue(0, ks0);
     for (int t = 0; t < ntiles; t += NSTAGE) {
