@@ -504,7 +504,7 @@ def both_roofs(F: float, B: float, kern_ms: float) -> dict:
 
 
 def device_facts(copy_bytes: int = 1 << 30, reps: int = 10) -> dict:
-    """What the box reports (name, compute units, architecture) and the HBM
+    """What the device reports (name, compute units, architecture) and the HBM
     bandwidth two plain copies of copy_bytes reach here (bytes read + written
     per second): torch's device copy, and the library's row gather
     (attn_sink_cp_permute_rows) with the identity index over 64 KB rows."""
