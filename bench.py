@@ -37,6 +37,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import math
 import os
@@ -127,10 +128,18 @@ def algorithmic_bytes(case) -> int:
     return int(b)
 
 
+def _code_only(text: str) -> str:
+    """Source text without comments and blank-line differences, so that a
+    comment edit does not count as a kernel change."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(ln.rstrip() for ln in text.splitlines() if ln.strip())
+
+
 def kernel_hash(kind: str) -> str:
     h = hashlib.sha256()
     for f in ("common.hpp", KERNEL_SRC[kind]):
-        h.update(open(os.path.join(ROOT, "sink_aware_masked_amd", "csrc", f), "rb").read())
+        h.update(_code_only(open(os.path.join(ROOT, "sink_aware_masked_amd", "csrc", f)).read()).encode())
     return h.hexdigest()[:16]
 
 

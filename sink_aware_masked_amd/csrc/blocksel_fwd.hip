@@ -71,7 +71,8 @@ void blocksel_fwd_bf16(const Params p) {
   const int bhi = qlast / BS;
   const uint8_t* tab = p.bsel + (int64_t)hidx * p.bsel_head;
 
-  // ---- per-lane columns: n-block nb holds queries q0 + 16*wave + 4*nb + [0,4)
+  // ---- per-lane columns: column block nb of this wave holds queries
+  // q0 + 4 NB_PER_WAVE wave + 4 nb + [0, 4), lane col their (col / 4, col % 4) pair
   int qi[NB_PER_WAVE], dstart[NB_PER_WAVE];
   const int hh = col & 3;
   const int h = kvh * G + hh;
