@@ -133,8 +133,12 @@ __device__ __forceinline__ void lds_barrier() {
 // Lazy rescaling: the running reference max only moves when a new logit
 // exceeds it by more than this (log2 units), so exp2(s - m) stays <= 2^8 and
 // the accumulator rescale (a pass over every accumulator register) is skipped
-// on almost every tile.  Exact: any reference works as long as the terms stay
-// in range; the final normalisation uses the same reference.
+// on almost every tile.  Exact in real arithmetic: any reference works as long
+// as the terms stay in range, and the final normalisation uses the same one.
+// Once P is rounded to bf16 for the P.V product it is not free: the largest
+// key's weight is exactly 1 only if the reference is the running max, so a
+// lazy reference adds that key's rounding error, which matters where a row
+// has few keys (the window kernel follows the max at every increase instead).
 constexpr float kRescaleLog2 = 8.0f;
 
 // max / sum over the four 16-lane groups holding the same MFMA column.  The

@@ -46,11 +46,15 @@ struct WinCfg {
   static constexpr int NB = (D + 31) / 32;       // 32-wide column blocks of O^T
   static constexpr int ROWB = NCH * 16;          // bytes per LDS row
   static constexpr int SLOT = 2 * KT * ROWB;     // K tile + V tile
-  static constexpr int NS = D == 64 ? 5 : D == 80 ? 4 : D == 96 ? 3 : 2;  // slots: <= 80 KB, 2 workgroups per CU
+  // resident workgroups per CU (one wave of each per SIMD).  Head dim 80 runs
+  // three with two slots each: its band of 4 tiles then takes two rounds, but
+  // a third workgroup hides more of each round's load wait than two more slots
+  static constexpr int WG = D == 80 ? 3 : 2;
+  static constexpr int NS = D == 64 ? 5 : D == 80 ? 2 : D == 96 ? 3 : 2;  // ring slots
   static constexpr int NPW = SLOT / 1024 / 4;    // 1 KB direct-to-LDS loads per wave per slot
   static constexpr bool ILV = (D == 80);         // keys two apart in one transposing read
   static_assert(NPW * 4 * 1024 == SLOT, "slot is a whole number of wave loads");
-  static_assert(NS * SLOT <= 80 * 1024, "two workgroups per CU");
+  static_assert(WG * NS * SLOT <= 160 * 1024, "WG workgroups' rings fit one CU's LDS");
   static_assert(BM * (D + 8) * 2 <= NS * SLOT, "output staging fits the ring");
 };
 
@@ -95,7 +99,7 @@ __device__ __forceinline__ float swap_halves_sum(float x) {
 }
 
 template <int D, int SINK>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WinCfg<D>::WG, WinCfg<D>::WG)))
 void window_fwd_bf16(const Params p) {
   using C = WinCfg<D>;
   static_assert(D % 16 == 0 && D <= 128, "head dim");
@@ -261,10 +265,16 @@ void window_fwd_bf16(const Params p) {
       bm[blk] = m;
     }
 
-    // online softmax, exp2 domain, lazy reference max
+    // online softmax, exp2 domain.  The reference follows the running max at
+    // every increase (no lazy threshold): the largest key so far then gets
+    // P = 1 exactly, and only smaller weights carry the bf16 rounding of P.
+    // With a lazy reference the dominant key of a short window row (up to
+    // 129 keys here, often one key with a fifth of the weight) is rounded
+    // too, which lifts the worst per-row error by about 30 %; the extra
+    // rescale passes cost about 2 % of the kernel time.
     const float mt = swap_halves_max(fmaxf(bm[0], bm[1]));
     const float mn = fmaxf(m2, mt);
-    const bool move = mn > m2 + kRescaleLog2;  // also m2 == -inf < mn
+    const bool move = mn > m2;  // also m2 == -inf < mn
     if (__ballot(move) != 0) {
       const float alpha = move ? exp2f_fast(m2 - mn) : 1.0f;
       if (move) m2 = mn;
@@ -314,12 +324,17 @@ void window_fwd_bf16(const Params p) {
   // of the round without further synchronisation, so no wave waits at a
   // barrier for another wave's share of a tile it does not need itself.
   // (A 64-key window on 128 rows is one round.)
+  // Tiles go through the rounds in the order 0, 2, 4, ..., 1, 3, ...: a
+  // wave's 32 rows need a run of consecutive tiles, so each round then holds
+  // about half of every wave's blocks rather than all of the first waves'.
+  const int nhalf = (ntiles + 1) >> 1;
+  auto tile_at = [&](int k) { return k < nhalf ? 2 * k : 2 * (k - nhalf) + 1; };
   bool first = true;
   for (int t0 = 0; t0 < ntiles; t0 += C::NS) {
     if (!first) lds_barrier();  // the previous round's slots are free
 #pragma unroll
     for (int u = 0; u < C::NS; ++u)
-      if (t0 + u < ntiles) issue(t0 + u, u);
+      if (t0 + u < ntiles) issue(tile_at(t0 + u), u);
     wait_vmcnt<0>();
     lds_barrier();
     if (first && neg_scale) {
@@ -332,7 +347,7 @@ void window_fwd_bf16(const Params p) {
     first = false;
 #pragma unroll
     for (int u = 0; u < C::NS; ++u)
-      if (t0 + u < ntiles) compute(t0 + u, u);
+      if (t0 + u < ntiles) compute(tile_at(t0 + u), u);
   }
 
   // ---- epilogue.  O^T leaves the accumulators as 4-element pieces of 32
