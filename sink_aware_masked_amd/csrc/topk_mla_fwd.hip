@@ -60,8 +60,11 @@ template <int SINK>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void topk_mla_fwd_bf16(const Params p) {
   using namespace mla;
-  __shared__ __attribute__((aligned(16))) bf16 ks0[TILE_EL];
-  __shared__ __attribute__((aligned(16))) bf16 ks1[TILE_EL];
+  // the two ring stages are one array: the output staging of the epilogue
+  // spans both
+  __shared__ __attribute__((aligned(16))) bf16 ring[NSTAGE * TILE_EL];
+  bf16* const ks0 = ring;
+  bf16* const ks1 = ring + TILE_EL;
   __shared__ int kidx[CHUNK];
   __shared__ int wsum[NW];
 
@@ -266,7 +269,7 @@ void topk_mla_fwd_bf16(const Params p) {
   constexpr int OS = DV + 8;
   lds_barrier();  // every wave is done with the ring
   bf16* ost = ks0 + wave * (HPW * OS);
-  static_assert(NW * HPW * OS <= 2 * TILE_EL, "staging fits the ring");
+  static_assert(NW * HPW * OS <= NSTAGE * TILE_EL, "staging fits the ring");
 #pragma unroll
   for (int n = 0; n < NDV; ++n) {
     bf16x4 o;

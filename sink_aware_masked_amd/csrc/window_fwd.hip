@@ -4,12 +4,14 @@
 // first key; DeepSeek-V4 sparse-MLA page: the null-logit fold after the key
 // loop).
 //
-// One workgroup = 128 consecutive packed query rows x one query head; 4 waves
-// of 32 rows.  The key band of the workgroup, [lo(first row), hi(last row)],
-// streams through LDS slots, 64 keys (K tile then V tile) per slot, filled by
-// direct-to-LDS loads a round of slots at a time: with a 64-key window the
-// whole band (256 keys) is one round, in flight at once.  Q goes straight to
-// VGPRs.  Per wave and 32-key block:
+// One workgroup = 4 waves of 32 consecutive packed query rows, arranged as
+// 4 / G row blocks x G query heads of one kv head: G = 1 (128 rows x one
+// head) unless the heads come in groups (GQA), where G = 4 (32 rows x four
+// heads of one group) or 2 shares the staged key band between the heads.
+// The key band of the workgroup, [lo(first row), hi(last row)], streams
+// through LDS slots, 64 keys (K tile then V tile) per slot, filled by
+// direct-to-LDS loads a round of slots at a time.  Q goes straight to VGPRs.
+// Per wave and 32-key block:
 //   S^T[key][row] = K[key][:] . Q[row][:]          (MFMA 32x32x16 bf16)
 // so every lane owns one query row and 16 of the block's keys; masking is two
 // integer compares against the row's window; the key-0 bias is one compare
@@ -39,7 +41,7 @@ __device__ __forceinline__ floatx16 mfma32x32(bf16x8 a, bf16x8 b, floatx16 c) {
 
 template <int D>
 struct WinCfg {
-  static constexpr int BM = 128;                 // query rows per workgroup (4 waves x 32)
+  static constexpr int BM = 128;                 // rows of output staging (4 waves x 32)
   static constexpr int KT = 64;                  // keys per ring slot
   static constexpr int NCH = D / 8;              // 16-byte chunks per row
   static constexpr int NQK = D / 16;             // 32x32x16 MFMAs per block for S^T
@@ -98,25 +100,29 @@ __device__ __forceinline__ float swap_halves_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int D, int SINK>
+template <int D, int SINK, int G>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WinCfg<D>::WG, WinCfg<D>::WG)))
 void window_fwd_bf16(const Params p) {
   using C = WinCfg<D>;
+  static_assert(G == 1 || G == 2 || G == 4, "heads per workgroup");
+  constexpr int BM = 32 * (4 / G);  // query rows per workgroup
   static_assert(D % 16 == 0 && D <= 128, "head dim");
   __shared__ __attribute__((aligned(1024))) unsigned char smem[C::NS * C::SLOT];
 
   const int b = xcd_remap(blockIdx.x, gridDim.x);
   // tile-major: the heads of one row tile are neighbours, so an XCD's L2
   // holds whole K/V rows (all heads) of a few consecutive tiles
-  const int tile = b / p.Hq;
-  const int h = b - tile * p.Hq;
-  const int kvh = h / p.group;
+  const int nhg = p.Hq / G;
+  const int tile = b / nhg;
+  const int hg = b - tile * nhg;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   const int n = lane & 31, hf = lane >> 5;                      // MFMA column (row of the wave), half
-  const int r0 = tile * C::BM;
-  const int rlast = min(r0 + C::BM - 1, p.T - 1);
-  const int r0w = r0 + 32 * wave;
+  const int h = G * hg + wave % G;       // this wave's query head
+  const int kvh = (G * hg) / p.group;    // the G heads share it: group % G == 0
+  const int r0 = tile * BM;
+  const int rlast = min(r0 + BM - 1, p.T - 1);
+  const int r0w = r0 + 32 * (wave / G);
   const bool wave_active = r0w <= rlast;
 
   // ---- windows.  Sequences touching this tile: sa .. sb (scalar loads only,
@@ -323,7 +329,8 @@ void window_fwd_bf16(const Params p) {
   // once; after one wait and one barrier every wave runs through its blocks
   // of the round without further synchronisation, so no wave waits at a
   // barrier for another wave's share of a tile it does not need itself.
-  // (A 64-key window on 128 rows is one round.)
+  // (The 256-key band of a 64-key window on 128 rows is one round for
+  // D = 64, two for D = 80.)
   // Tiles go through the rounds in the order 0, 2, 4, ..., 1, 3, ...: a
   // wave's 32 rows need a run of consecutive tiles, so each round then holds
   // about half of every wave's blocks rather than all of the first waves'.
@@ -389,23 +396,34 @@ void window_fwd_bf16(const Params p) {
 
 // Work items of one launch (workgroups x 256 lanes); every head dim uses
 // 128-row tiles.
+static int window_heads_per_wg(int group) { return group % 4 == 0 ? 4 : group % 2 == 0 ? 2 : 1; }
+
 int64_t window_bf16_items(const Params& p) {
-  static_assert(WinCfg<64>::BM == 128 && WinCfg<80>::BM == 128 && WinCfg<96>::BM == 128 &&
-                WinCfg<128>::BM == 128, "one tile height");
-  return ((int64_t)p.T + 127) / 128 * p.Hq * 256;
+  const int g = window_heads_per_wg(p.group), bm = 32 * (4 / g);
+  return ((int64_t)p.T + bm - 1) / bm * (p.Hq / g) * 256;
+}
+
+template <int D, int G>
+static hipError_t launch_window_dg(const Params& p, int sink, hipStream_t st) {
+  Params q = p;
+  constexpr int BM = 32 * (4 / G);
+  q.num_tiles = (p.T + BM - 1) / BM;
+  const dim3 grid((unsigned)(q.num_tiles * (p.Hq / G))), block(256);
+  switch (sink) {
+    case kSinkNone: hipLaunchKernelGGL((window_fwd_bf16<D, kSinkNone, G>), grid, block, 0, st, q); break;
+    case kSinkKey0: hipLaunchKernelGGL((window_fwd_bf16<D, kSinkKey0, G>), grid, block, 0, st, q); break;
+    default: hipLaunchKernelGGL((window_fwd_bf16<D, kSinkNull, G>), grid, block, 0, st, q); break;
+  }
+  return hipGetLastError();
 }
 
 template <int D>
 static hipError_t launch_window_d(const Params& p, int sink, hipStream_t st) {
-  Params q = p;
-  q.num_tiles = (p.T + WinCfg<D>::BM - 1) / WinCfg<D>::BM;
-  const dim3 grid((unsigned)(q.num_tiles * p.Hq)), block(256);
-  switch (sink) {
-    case kSinkNone: hipLaunchKernelGGL((window_fwd_bf16<D, kSinkNone>), grid, block, 0, st, q); break;
-    case kSinkKey0: hipLaunchKernelGGL((window_fwd_bf16<D, kSinkKey0>), grid, block, 0, st, q); break;
-    default: hipLaunchKernelGGL((window_fwd_bf16<D, kSinkNull>), grid, block, 0, st, q); break;
+  switch (window_heads_per_wg(p.group)) {
+    case 4: return launch_window_dg<D, 4>(p, sink, st);
+    case 2: return launch_window_dg<D, 2>(p, sink, st);
+    default: return launch_window_dg<D, 1>(p, sink, st);
   }
-  return hipGetLastError();
 }
 
 hipError_t launch_window_bf16(const Params& p, int sink, hipStream_t st) {
