@@ -265,20 +265,30 @@ void blocksel_fwd_bf16(const Params p) {
           }
       }
       lsum[nb] += ps;
+      // P of the two 32-key halves, then the 16 P.V MFMAs as one sequence
+      // with the V^T operands one block ahead of the MFMAs that use them.
+      // Written out on purpose: at this kernel's 128-register budget the
+      // compiler otherwise reads each operand right before its MFMA and
+      // waits for it there, so every MFMA paid a full LDS round trip.
+      bf16x8 pbh[2];
 #pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2) {
-        bf16x8 pb;
+      for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          pb[e] = static_cast<bf16>(s[2 * c2][e]);
-          pb[4 + e] = static_cast<bf16>(s[2 * c2 + 1][e]);
+          pbh[c2][e] = static_cast<bf16>(s[2 * c2][e]);
+          pbh[c2][4 + e] = static_cast<bf16>(s[2 * c2 + 1][e]);
         }
-        const bf16* v0 = vs + c2 * 2048;
+      auto vld = [&](int k) {
+        const bf16* v0 = vs + (k >> 3) * 2048 + voff[k & 7];
+        return cat8(lds_read_tr4(v0), lds_read_tr4(v0 + 1024));
+      };
+      bf16x8 va = vld(0);
 #pragma unroll
-        for (int n = 0; n < NDV; ++n) {
-          const bf16x8 va = cat8(lds_read_tr4(v0 + voff[n]), lds_read_tr4(v0 + 1024 + voff[n]));
-          acc[nb][n] = mfma32(va, pb, acc[nb][n]);
-        }
+      for (int k = 0; k < 2 * NDV; ++k) {
+        bf16x8 vn = va;
+        if (k + 1 < 2 * NDV) vn = vld(k + 1);
+        acc[nb][k & 7] = mfma32(va, pbh[k >> 3], acc[nb][k & 7]);
+        va = vn;
       }
     }
   };
