@@ -366,30 +366,29 @@ void blocksel_fwd_bf16(const Params p) {
     // every wave is done with pair r - 1, whose stages then take pair r + 1
     // while pair r is computed.  Between barriers a wave runs through both
     // blocks, so a wave whose queries chose neither block of a pair costs the
-    // others one barrier instead of two.  Waves 0-7 issue their share of the
-    // next pair right after the barrier and waves 8-15 after their first
-    // block, so the waves of a SIMD start the pair in two phases (some in
-    // their MFMAs while the others issue loads) and the loads of a pair reach
-    // the memory pipeline in two halves (2-3 % faster than all at once).
+    // others one barrier instead of two.  Every wave issues its share of
+    // the next pair after its first block of the current one: each pair
+    // starts straight into compute, and the loads reach the memory pipeline
+    // spread over the pair as the waves finish their first blocks (3-4 %
+    // faster than issuing right after the barrier in half of the waves or in
+    // all of them).
     const int npair = (nbl + 1) >> 1;
     auto issue_pair = [&](int r) {
 #pragma unroll
       for (int u = 0; u < 2; ++u)
         if (2 * r + u < nbl) issue(blist[2 * r + u], kvs + ((r & 1) * 2 + u) * 2 * TILE_EL);
     };
-    const bool late = (wave & 8) != 0;  // wave-uniform
     issue_pair(0);
     for (int r = 0; r < npair; ++r) {
       wait_vmcnt<0>();
       lds_barrier();
-      if (!late && r + 1 < npair) issue_pair(r + 1);
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         if (2 * r + u < nbl) {
           const int blk = blist[2 * r + u];
           compute(blk, (blk >> 5) - wb, kvs + ((r & 1) * 2 + u) * 2 * TILE_EL);
         }
-        if (u == 0 && late && r + 1 < npair) issue_pair(r + 1);
+        if (u == 0 && r + 1 < npair) issue_pair(r + 1);
       }
     }
   }
