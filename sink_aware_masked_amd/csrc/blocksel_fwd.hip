@@ -54,8 +54,12 @@ void blocksel_fwd_bf16(const Params p) {
   __shared__ int blist[32 * MAXW];
   __shared__ int nblist;
 
+  // Each XCD takes a contiguous range of b (one kv head's tiles on this
+  // shape).  Its tiles go last first: a tile's work grows with its position
+  // in the document (the union of earlier blocks), so the long workgroups
+  // start early and the short ones fill the end of the launch (2-3 %).
   const int b = xcd_remap(blockIdx.x, gridDim.x);
-  const int tile = b % p.num_tiles;
+  const int tile = p.num_tiles - 1 - b % p.num_tiles;
   const int kvh = b / p.num_tiles;
   const int hidx = kvh / (p.Hkv / p.Hidx);
   const int tid = threadIdx.x, lane = tid & 63;
