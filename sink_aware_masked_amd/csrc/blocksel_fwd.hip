@@ -38,8 +38,8 @@ constexpr int RCH = D / 8;      // 16 16-byte chunks per row
 constexpr int TILE_EL = BS * D; // bf16 elements of one K (or V) block
 constexpr int LDPW = BS * RCH / 64 / NW;  // 1 direct-to-LDS load per wave per tensor
 constexpr int MAXW = 32;        // selection words per query held in LDS per pass (1024 blocks)
-constexpr int NSTAGE = 4;       // LDS ring depth: three blocks in flight behind the one computed
-static_assert(NSTAGE >= 2 && NSTAGE <= 4, "the in-flight wait below covers up to two later blocks");
+constexpr int NSTAGE = 4;       // LDS ring: the pair of blocks computed and the pair in flight
+static_assert(NSTAGE == 4, "pair r uses stages 2 (r % 2) and 2 (r % 2) + 1");
 }  // namespace bsel
 
 // 16 waves of 4 queries x 4 heads each, held to 128 registers, so four waves
