@@ -159,11 +159,17 @@ void mla_decode_fp8_partial(const DecodeParams p) {
     // count re-read a valid row (finite; their logits are masked).
     float sc_reg = 0.0f;
     auto issue = [&](int t, int stage) {
+      // The per-load offsets are recomputed here from an opaque copy of the
+      // lane id: hoisted out of the tile loop they are spilled, and reloading
+      // a spilled offset waits for every vector load before it -- the
+      // previous gathers of the tile -- so the gathers ran one at a time.
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
 #pragma unroll
       for (int k = 0; k < (F8_LOADS + NW - 1) / NW; ++k) {
         const int q = wave + NW * k;
         if (q < F8_LOADS) {  // wave-uniform
-          const int byte = 1024 * q + 16 * lane;
+          const int byte = 1024 * q + 16 * ln;
           const int r = byte / ROWB, off = byte - r * ROWB;
           const int posr = t * KT + r;
           const int j = kidx[posr < nvalid ? posr : 0];
