@@ -125,8 +125,20 @@ void window_fwd_bf16(const Params p) {
   const int r0w = r0 + 32 * (wave / G);
   const bool wave_active = r0w <= rlast;
 
-  // ---- windows.  Sequences touching this tile: sa .. sb (scalar loads only,
-  // so no vector load is pending once the ring is in flight).
+  // Q^T fragments (B operand) straight to VGPRs: lane (n, hf) holds row
+  // r0w + n, dims 16 d + 8 hf + [0, 8).  Issued first: the rows do not
+  // depend on the sequences, so the loads are in flight during the searches
+  // below.
+  const char* qg = static_cast<const char*>(p.q) + (int64_t)h * p.q_head * 2;
+  const int64_t qrow = p.q_row * 2;
+  bf16x8 qf[C::NQK];
+  {
+    const char* qr = qg + (int64_t)min(r0w + n, rlast) * qrow;
+#pragma unroll
+    for (int d = 0; d < C::NQK; ++d) qf[d] = *reinterpret_cast<const bf16x8*>(qr + 32 * d + 16 * hf);
+  }
+
+  // ---- windows.  Sequences touching this tile: sa .. sb (scalar loads).
   const int sa = find_segment(p.cu, p.num_seqs, r0);
   const int sb = find_segment(p.cu, p.num_seqs, rlast);
   // bounds as offsets that cannot overflow: max(start, r - W) = r - min(W, r - start)
@@ -162,8 +174,7 @@ void window_fwd_bf16(const Params p) {
   // 1024 i + 16 l, i.e. physical chunk q = 64 i + l of the slot.
   const char* kg = static_cast<const char*>(p.k) + (int64_t)kvh * p.k_head * 2;
   const char* vg = static_cast<const char*>(p.v) + (int64_t)kvh * p.v_head * 2;
-  const char* qg = static_cast<const char*>(p.q) + (int64_t)h * p.q_head * 2;
-  const int64_t krow = p.k_row * 2, vrow = p.v_row * 2, qrow = p.q_row * 2;
+  const int64_t krow = p.k_row * 2, vrow = p.v_row * 2;
   const uint32_t sbase = lds_addr(smem);
   int trow[C::NPW], tc16[C::NPW];  // per load: row inside the tile, source chunk byte offset
 #pragma unroll
@@ -187,14 +198,6 @@ void window_fwd_bf16(const Params p) {
       load_lds16_m0(g, sbase + slot * C::SLOT + 1024 * i);
     }
   };
-  // Q^T fragments (B operand) straight to VGPRs: lane (n, hf) holds row
-  // r0w + n, dims 16 d + 8 hf + [0, 8).
-  bf16x8 qf[C::NQK];
-  {
-    const char* qr = qg + (int64_t)min(r0w + n, rlast) * qrow;
-#pragma unroll
-    for (int d = 0; d < C::NQK; ++d) qf[d] = *reinterpret_cast<const bf16x8*>(qr + 32 * d + 16 * hf);
-  }
   // ---- per-lane LDS read offsets (bytes, relative to a slot)
   constexpr int KSTEP = C::ILV ? 2 : 1;
   const int kr = (n & ~7) | key_in8<D>(n & 7);  // K row of MFMA row n in a 32-key block
