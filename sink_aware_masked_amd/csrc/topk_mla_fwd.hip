@@ -189,6 +189,7 @@ void topk_mla_fwd_bf16(const Params p) {
           const int nx = cc + KPIPE;
           if (nx < NQC)
             kb[cc % KPIPE] = *reinterpret_cast<const bf16x8*>(krow + ((nx & 1) ? kofs_o : kofs_e) + 2048 * (nx >> 1));
+          asm volatile("" ::: "memory");  // keeps each read KPIPE MFMAs ahead of its use
         }
         const bool all_in = t0 + 16 * sb + 4 * grp + 3 < nvalid;
 #pragma unroll
