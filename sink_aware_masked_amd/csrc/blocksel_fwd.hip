@@ -193,15 +193,26 @@ void blocksel_fwd_bf16(const Params p) {
       // scale, the key-0 bias and the reference max go into one fma in the
       // exponent, so a zero bias gives bit for bit the no-sink numbers
       float s[4][4];
+      // The 16 K operands of the unit (4 key sub-blocks x 4 head-dim
+      // chunks), read KP MFMAs ahead of their use.  The empty asm with a
+      // memory clobber after each read keeps the scheduler from sinking the
+      // reads back next to their MFMAs, which at this register budget it
+      // otherwise does (one or two reads in flight).
+      constexpr int KP = 4;
+      auto kld = [&](int k) { return *reinterpret_cast<const bf16x8*>(ks + (k >> 2) * 1024 + koff[k & 3]); };
+      bf16x8 kb[KP];
 #pragma unroll
-      for (int sb = 0; sb < 4; ++sb) {
-        floatx4 a = {0.f, 0.f, 0.f, 0.f};
-        const bf16* krow = ks + sb * 1024;
+      for (int k = 0; k < KP; ++k) kb[k] = kld(k);
+      floatx4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int cc = 0; cc < NQC; ++cc)
-          a = mfma32(*reinterpret_cast<const bf16x8*>(krow + koff[cc]), qf[nb][cc], a);
+      for (int k = 0; k < 16; ++k) {
+        a = mfma32(kb[k % KP], qf[nb][k & 3], (k & 3) ? a : floatx4{0.f, 0.f, 0.f, 0.f});
+        if (k + KP < 16) kb[k % KP] = kld(k + KP);
+        asm volatile("" ::: "memory");
+        if ((k & 3) == 3) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) s[sb][e] = a[e];
+          for (int e = 0; e < 4; ++e) s[k >> 2][e] = a[e];
+        }
       }
       // Elementwise masks only where some selected column sees causality or a
       // document start (or the key-0 bias); otherwise a column's selection
@@ -270,10 +281,10 @@ void blocksel_fwd_bf16(const Params p) {
       }
       lsum[nb] += ps;
       // P of the two 32-key halves, then the 16 P.V MFMAs as one sequence
-      // with the V^T operands one block ahead of the MFMAs that use them.
-      // Written out on purpose: at this kernel's 128-register budget the
-      // compiler otherwise reads each operand right before its MFMA and
-      // waits for it there, so every MFMA paid a full LDS round trip.
+      // with the V^T operands VP MFMAs ahead of their use, pinned as the K
+      // reads are: left to itself the compiler reads each operand right
+      // before its MFMA and waits for it there, so every MFMA paid a full
+      // LDS round trip.
       bf16x8 pbh[2];
 #pragma unroll
       for (int c2 = 0; c2 < 2; ++c2)
@@ -286,13 +297,16 @@ void blocksel_fwd_bf16(const Params p) {
         const bf16* v0 = vs + (k >> 3) * 2048 + voff[k & 7];
         return cat8(lds_read_tr4(v0), lds_read_tr4(v0 + 1024));
       };
-      bf16x8 va = vld(0);
+      constexpr int VP = 2;  // V^T operands VP MFMAs ahead
+      bf16x8 vb[VP];
+#pragma unroll
+      for (int k = 0; k < VP; ++k) vb[k] = vld(k);
 #pragma unroll
       for (int k = 0; k < 2 * NDV; ++k) {
-        bf16x8 vn = va;
-        if (k + 1 < 2 * NDV) vn = vld(k + 1);
+        const bf16x8 va = vb[k % VP];
+        if (k + VP < 2 * NDV) vb[k % VP] = vld(k + VP);
         acc[nb][k & 7] = mfma32(va, pbh[k >> 3], acc[nb][k & 7]);
-        va = vn;
+        asm volatile("" ::: "memory");
       }
     }
   };
