@@ -126,10 +126,17 @@ void blocksel_fwd_bf16(const Params p) {
   const float sl2 = fmaxf(fabsf(p.scale_log2), __FLT_MIN__);
   const float bias2 = (SINK == kSinkKey0) ? __ldg(p.sinks + h) * kLog2e : 0.0f;
   float m2[NB_PER_WAVE], lsum[NB_PER_WAVE];
+  // Kept beside the reference max m2 (updated only when it moves): thr, the
+  // rescale threshold m2 + kRescaleLog2 on the raw (unscaled) logits, and
+  // nmu, the exponent offset -m2 (0 while m2 is -inf)
+  float thr[NB_PER_WAVE], nmu[NB_PER_WAVE];
+  const float inv_sl2 = 1.0f / sl2;
   floatx4 acc[NB_PER_WAVE][NDV];
 #pragma unroll
   for (int nb = 0; nb < NB_PER_WAVE; ++nb) {
     m2[nb] = kNegInf;
+    thr[nb] = kNegInf;
+    nmu[nb] = 0.0f;
     lsum[nb] = 0.0f;
 #pragma unroll
     for (int n = 0; n < NDV; ++n) acc[nb][n] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -174,7 +181,9 @@ void blocksel_fwd_bf16(const Params p) {
   };
 
   // ---- one staged block for this wave's column blocks
-  auto compute = [&](int blk, int wsel, const bf16* st) {
+  auto compute = [&](int blk_, int wb, const bf16* st) {
+    const int blk = __builtin_amdgcn_readfirstlane(blk_);  // wave-uniform: scalar arithmetic
+    const int wsel = (blk >> 5) - wb;
     const int kb0 = blk * BS;
     const bf16* ks = st;
     const bf16* vs = st + TILE_EL;
@@ -182,12 +191,15 @@ void blocksel_fwd_bf16(const Params p) {
     for (int nb = 0; nb < NB_PER_WAVE; ++nb) {
       const int ql = 4 * NB_PER_WAVE * wave + 4 * nb + (col >> 2);
       const bool sel = (qbits[ql][wsel] >> (blk & 31)) & 1u;
-      if (__ballot(sel) == 0) continue;  // none of the 4 queries picked this block
-      // is the whole block causal and inside the document for every column?
-      const bool whole = (kb0 >= dstart[nb]) & (kb0 + BS - 1 <= qi[nb]);
-      const bool edge = __ballot(sel & !whole) != 0;
+      const uint64_t selm = __ballot(sel);
+      if (selm == 0) continue;  // none of the 4 queries picked this block
+      // Wave-uniform tests below are ballots of plain compares masked by
+      // selm (scalar ands; a ballot of a compound condition costs two VALU
+      // instructions more).  Is the whole block causal and inside the
+      // document for every selected column?
+      const bool edge = ((__ballot(kb0 < dstart[nb]) | __ballot(kb0 + BS - 1 > qi[nb])) & selm) != 0;
       const bool has_key0 =
-          SINK == kSinkKey0 && __ballot(sel & (dstart[nb] >= kb0) & (dstart[nb] < kb0 + BS)) != 0;
+          SINK == kSinkKey0 && (__ballot((dstart[nb] >= kb0) & (dstart[nb] < kb0 + BS)) & selm) != 0;
 
       // s keeps the raw dot products (unselected / masked ones -inf); the
       // scale, the key-0 bias and the reference max go into one fma in the
@@ -234,49 +246,56 @@ void blocksel_fwd_bf16(const Params p) {
       }
       const int dk = dstart[nb] - kb0 - 4 * grp;  // key-0 column of this lane, as 16 sb + e
       float mt = kNegInf;
+      bool need;  // some column's max passed its threshold (wave-uniform)
       if (has_key0) {
 #pragma unroll
         for (int sb = 0; sb < 4; ++sb)
 #pragma unroll
           for (int e = 0; e < 4; ++e)
             mt = fmaxf(mt, __builtin_fmaf(s[sb][e], sl2, (16 * sb + e == dk) ? bias2 : 0.0f));
+        need = __ballot(mt > m2[nb] + kRescaleLog2) != 0;
       } else {
 #pragma unroll
         for (int sb = 0; sb < 4; ++sb)
 #pragma unroll
           for (int e = 0; e < 4; ++e) mt = fmaxf(mt, s[sb][e]);
-        mt = sel ? mt * sl2 : kNegInf;  // sl2 > 0: the max commutes with the scaling
+        // raw logits against the raw threshold (sl2 > 0; where rounding
+        // makes the two forms disagree only the timing of a rescale moves)
+        need = (__ballot(mt > thr[nb]) & selm) != 0;
       }
-      mt = max_over_groups(mt);
-      if (__ballot(mt > m2[nb] + kRescaleLog2) != 0) {  // lazy rescale (wave-uniform)
-        const float mn = fmaxf(m2[nb], mt);
+      // lazy rescale: a column's max passes the threshold iff one of its four
+      // lanes' partial maxima does, so the lanes' exchange is only needed here
+      if (need) {
+        if (!has_key0) mt = sel ? mt * sl2 : kNegInf;
+        const float mn = fmaxf(m2[nb], max_over_groups(mt));
         const float alpha = (m2[nb] == mn) ? 1.0f : exp2f_fast(m2[nb] - mn);
         lsum[nb] *= alpha;
 #pragma unroll
         for (int n = 0; n < NDV; ++n) acc[nb][n] *= alpha;
         m2[nb] = mn;
+        thr[nb] = (mn + kRescaleLog2) * inv_sl2;
+        nmu[nb] = (mn == kNegInf) ? 0.0f : -mn;
       }
-      const float mu = (m2[nb] == kNegInf) ? 0.0f : m2[nb];
-      float ps = 0.0f;
+      float ps;
       if (has_key0) {
-        const float bmu = bias2 - mu;
+        const float bmu = bias2 + nmu[nb];
 #pragma unroll
         for (int sb = 0; sb < 4; ++sb)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            s[sb][e] = exp2f_fast(__builtin_fmaf(s[sb][e], sl2, (16 * sb + e == dk) ? bmu : -mu));
-            ps += s[sb][e];
+            s[sb][e] = exp2f_fast(__builtin_fmaf(s[sb][e], sl2, (16 * sb + e == dk) ? bmu : nmu[nb]));
+            ps = (sb | e) ? ps + s[sb][e] : s[sb][e];
           }
       } else {
         // masked elements are already -inf (scale sl2 keeps them so); on
         // unmasked blocks an unselected column takes scale 0 and offset -inf
-        const float ks = (edge | sel) ? sl2 : 0.0f, ko = (edge | sel) ? -mu : kNegInf;
+        const float ks = (edge | sel) ? sl2 : 0.0f, ko = (edge | sel) ? nmu[nb] : kNegInf;
 #pragma unroll
         for (int sb = 0; sb < 4; ++sb)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             s[sb][e] = exp2f_fast(__builtin_fmaf(s[sb][e], ks, ko));
-            ps += s[sb][e];
+            ps = (sb | e) ? ps + s[sb][e] : s[sb][e];
           }
       }
       lsum[nb] += ps;
@@ -403,8 +422,7 @@ void blocksel_fwd_bf16(const Params p) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         if (2 * r + u < nbl) {
-          const int blk = blist[2 * r + u];
-          compute(blk, (blk >> 5) - wb, kvs + ((r & 1) * 2 + u) * 2 * TILE_EL);
+          compute(blist[2 * r + u], wb, kvs + ((r & 1) * 2 + u) * 2 * TILE_EL);
         }
         if (u == 0 && r + 1 < npair) issue_pair(r + 1);
       }

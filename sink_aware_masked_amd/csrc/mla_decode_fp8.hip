@@ -212,9 +212,10 @@ void mla_decode_fp8_partial(const DecodeParams p) {
       for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
         for (int e = 0; e < 4; ++e) mt = fmaxf(mt, s[sb][e]);
-      mt = max_over_groups(mt);
+      // the lanes' maxima are exchanged only on the rescale path: a column
+      // passes the threshold iff one of its lanes does
       if (__ballot(mt > m2 + kRescaleLog2) != 0) {
-        const float mn = fmaxf(m2, mt);
+        const float mn = fmaxf(m2, max_over_groups(mt));
         const float alpha = (m2 == mn) ? 1.0f : exp2f_fast(m2 - mn);
         lsum *= alpha;
 #pragma unroll

@@ -201,9 +201,10 @@ void topk_mla_fwd_bf16(const Params p) {
       for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
         for (int e = 0; e < 4; ++e) mt = fmaxf(mt, s[sb][e]);
-      mt = max_over_groups(mt);
-      if (__ballot(mt > m2 + kRescaleLog2) != 0) {  // lazy rescale (wave-uniform)
-        const float mn = fmaxf(m2, mt);
+      // lazy rescale (wave-uniform; the lanes' maxima are exchanged only on
+      // that path: a column passes the threshold iff one of its lanes does)
+      if (__ballot(mt > m2 + kRescaleLog2) != 0) {
+        const float mn = fmaxf(m2, max_over_groups(mt));
         const float alpha = (m2 == mn) ? 1.0f : exp2f_fast(m2 - mn);
         lsum *= alpha;
 #pragma unroll
