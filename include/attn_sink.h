@@ -152,7 +152,9 @@ typedef struct attn_mask_arg {
  *   mask_kind  attn_mask_kind;  mask: its parameters (host struct)
  *   sinks      device f32 [Hq]; required unless sink_mode == ATTN_SINK_NONE
  *   sink_mode  attn_sink_mode
- *   scale      multiplies q.k before the sink is applied (e.g. 1/sqrt(Dqk))
+ *   scale      multiplies q.k before the sink is applied (e.g. 1/sqrt(Dqk));
+ *              must be finite with scale * log2(e) finite (|scale| < ~2.36e38),
+ *              else ATTN_ERR_RANGE
  *   out        [T, Hq, Dv]    same dtype as q; must not overlap any input
  *   lse        device f32, dense [Hq, T]; must not overlap any input
  *   stream     HIP stream the kernel is enqueued on (0 = null stream)

@@ -52,6 +52,13 @@ int elem_size(int32_t dt) {
 
 bool valid_dtype(int32_t dt) { return dt >= ATTN_DTYPE_BF16 && dt <= ATTN_DTYPE_FP8_E4M3; }
 
+// A usable scale is finite and so is scale * log2(e), the factor the kernels
+// apply in the exp2 domain (|scale| below about 2.36e38).
+bool scale_ok(float scale) {
+  const float s2 = scale * attn::kLog2e;
+  return scale == scale && s2 - s2 == 0.0f;
+}
+
 // Rank, non-negative sizes / strides, unit inner stride.
 // A NULL data pointer is accepted only for an empty tensor.
 int check_tensor(const attn_tensor* t, int ndim) {
@@ -114,8 +121,7 @@ int prepare(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
   if (!lse && T > 0) return ATTN_ERR_NULL;
   if (reinterpret_cast<uintptr_t>(lse) % 4 != 0) return ATTN_ERR_STRIDE;
   if (sink_mode != ATTN_SINK_NONE && !sinks) return ATTN_ERR_NULL;
-  if (!(scale == scale) || scale == __builtin_huge_valf() || scale == -__builtin_huge_valf())
-    return ATTN_ERR_RANGE;
+  if (!scale_ok(scale)) return ATTN_ERR_RANGE;
 
   memset(P, 0, sizeof(*P));
   P->q = q->data; P->k = k->data; P->v = v->data; P->out = out->data;
@@ -265,8 +271,7 @@ int prepare_key0(const attn_tensor* q, const attn_tensor* k, const attn_tensor* 
   if (window > T) window = (int32_t)T;  // rows past T do not exist: same affected rows
   // one 256-lane workgroup per (row slot, group of 4 heads)
   if ((int64_t)num_seqs * ((int64_t)window + 1) * 256 > kMaxGridItems) return ATTN_ERR_RANGE;
-  if (!(scale == scale) || scale == __builtin_huge_valf() || scale == -__builtin_huge_valf())
-    return ATTN_ERR_RANGE;
+  if (!scale_ok(scale)) return ATTN_ERR_RANGE;
   memset(P, 0, sizeof(*P));
   P->q = q->data; P->k = k->data; P->v = v->data; P->out = out->data;
   P->lse = const_cast<float*>(lse);
@@ -545,7 +550,7 @@ int prepare_decode(const attn_tensor* q, const attn_tensor* kv, const float* kv_
     return ATTN_ERR_STRIDE;
   if (!lse && T > 0) return ATTN_ERR_NULL;
   if (reinterpret_cast<uintptr_t>(lse) % 4 != 0) return ATTN_ERR_STRIDE;
-  if (!(scale == scale) || scale == __builtin_huge_valf() || scale == -__builtin_huge_valf()) return ATTN_ERR_RANGE;
+  if (!scale_ok(scale)) return ATTN_ERR_RANGE;
   if (T * (Hq / 64) * 256 > kMaxGridItems) return ATTN_ERR_RANGE;  // one 256-lane workgroup per (row, 64 heads, piece)
   const int nsplit = attn::decode_splits(T, Hq, ti->shape[1]);
   if (T > 0 && (!ws || ws_bytes < decode_ws_bytes(T, Hq, nsplit))) return ws ? ATTN_ERR_RANGE : ATTN_ERR_NULL;

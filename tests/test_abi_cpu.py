@@ -139,6 +139,8 @@ def test_rejections(sam):
     _bad(E, w, "ATTN_ERR_STRIDE", q=torch.empty(256, 16, 84, dtype=torch.bfloat16)[:, :, :80])
     _bad(E, w, "ATTN_ERR_RANGE", mask={"window": -1})
     _bad(E, w, "ATTN_ERR_RANGE", scale=float("nan"))
+    _bad(E, w, "ATTN_ERR_RANGE", scale=3.0e38)   # finite, but scale * log2(e) overflows
+    _bad(E, w, "ATTN_ERR_RANGE", scale=-3.0e38)
     _bad(E, w, "ATTN_ERR_UNSUPPORTED", **{k_: torch.empty(256, h, 48, dtype=torch.bfloat16)
                                          for k_, h in (("q", 16), ("k", 4), ("v", 4), ("out", 16))})
     m = mla_args()
@@ -189,7 +191,7 @@ def test_key0_correct_validation(sam):
     a = key0_args()
     for over, expect in (({"sinks": None}, "ATTN_ERR_NULL"), ({"cu_seqlens": None}, "ATTN_ERR_NULL"),
                          ({"lse": None}, "ATTN_ERR_NULL"), ({"window": -1}, "ATTN_ERR_RANGE"),
-                         ({"scale": float("inf")}, "ATTN_ERR_RANGE"),
+                         ({"scale": float("inf")}, "ATTN_ERR_RANGE"), ({"scale": 3.0e38}, "ATTN_ERR_RANGE"),
                          ({"out": torch.empty(256, 16, 80, dtype=torch.float32)}, "ATTN_ERR_DTYPE"),
                          ({"k": torch.empty(255, 4, 80, dtype=torch.bfloat16)}, "ATTN_ERR_SHAPE"),
                          ({"k": torch.empty(256, 3, 80, dtype=torch.bfloat16),
@@ -315,7 +317,7 @@ def test_decode_validation(sam):
                          ({"kv_scale": None}, "ATTN_ERR_NULL"),
                          ({"out": torch.empty(8, 64, 576, dtype=torch.bfloat16)}, "ATTN_ERR_UNSUPPORTED"),
                          ({"topk_idx": torch.empty(9, 32, dtype=torch.int32)}, "ATTN_ERR_SHAPE"),
-                         ({"scale": float("nan")}, "ATTN_ERR_RANGE")):
+                         ({"scale": float("nan")}, "ATTN_ERR_RANGE"), ({"scale": -3.0e38}, "ATTN_ERR_RANGE")):
         b = decode_args()
         b.update(over)
         assert sam.STATUS[decode_check(sam, b)] == expect, (over.keys(), expect)
