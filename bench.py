@@ -137,9 +137,15 @@ def _code_only(text: str) -> str:
 
 
 def kernel_hash(kind: str) -> str:
+    """Hash of the kernel's code (comments ignored) and of the extra compiler
+    options its source is built with."""
+    from __graft_entry__ import EXTRA_FLAGS
     h = hashlib.sha256()
     for f in ("common.hpp", KERNEL_SRC[kind]):
         h.update(_code_only(open(os.path.join(ROOT, "sink_aware_masked_amd", "csrc", f)).read()).encode())
+    extra = EXTRA_FLAGS.get(KERNEL_SRC[kind])
+    if extra:
+        h.update(" ".join(extra).encode())
     return h.hexdigest()[:16]
 
 
