@@ -210,7 +210,7 @@ void blocksel_fwd_bf16(const Params p) {
       // memory clobber after each read keeps the scheduler from sinking the
       // reads back next to their MFMAs, which at this register budget it
       // otherwise does (one or two reads in flight).
-      constexpr int KP = 4;
+      constexpr int KP = 3;
       auto kld = [&](int k) { return *reinterpret_cast<const bf16x8*>(ks + (k >> 2) * 1024 + koff[k & 3]); };
       bf16x8 kb[KP];
 #pragma unroll
