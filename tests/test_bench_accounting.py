@@ -74,3 +74,24 @@ def test_bench_refuses_more_than_one_gpu(capsys):
     """One GPU only: --gpus above 1 exits with status 2 and says why."""
     assert bench.main(["--gpus", "2"]) == 2
     assert "one GPU only" in capsys.readouterr().err
+
+
+def test_extra_compiler_options_name_existing_sources():
+    """Per-source compiler options apply only to files that exist, so a
+    renamed kernel source cannot silently lose its options."""
+    import os
+    import __graft_entry__ as g
+    for name, flags in g.EXTRA_FLAGS.items():
+        assert os.path.exists(os.path.join(g.CSRC, name)), name
+        assert flags and all(isinstance(f, str) for f in flags)
+
+
+def test_traffic_record_is_keyed_to_source_and_options(monkeypatch):
+    """The committed PMC traffic of a kernel is used only for the source and
+    the compiler options it was measured on."""
+    import __graft_entry__ as g
+    base = bench.kernel_hash("blocksel")
+    monkeypatch.setitem(g.EXTRA_FLAGS, "blocksel_fwd.hip", ["-O2"])
+    assert bench.kernel_hash("blocksel") != base
+    monkeypatch.delitem(g.EXTRA_FLAGS, "blocksel_fwd.hip")
+    assert bench.kernel_hash("blocksel") != base
